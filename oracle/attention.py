@@ -1,0 +1,208 @@
+"""Materialised exact attention in float64 -- the oracle's definition.
+
+Test infrastructure only (see the package docstring).  Nothing here is blocked,
+fused or reordered beyond computing whole query rows a few at a time: every
+query row is produced from the full score row, exactly as written on the pages.
+
+Definition followed (per batch b, head h; or per packed sequence s, head h):
+  S = scale * Q K^T                      [P2 §1.1; P4 §18.2.1]
+  masked entries of S are -inf           [P4 §18.2.2 item 3 (causal, j <= i kept),
+                                          item 4 (padding masks act on keys)]
+  P = row-softmax(S), O = P V            [P2 §1.1, §3.2 safe softmax]
+  LSE_i = log sum_j exp(S_ij)            [P1 §三 end ("保存 logsumexp"); P3 §04]
+  D_i  = rowsum(dO o O)                  [P1 §5.2]
+  dP = dO V^T, dS = P o (dP - D)         [P1 §5.1-5.2; P4 §18.2.4]
+  dV = P^T dO, dQ = scale dS K,
+  dK = scale dS^T Q                      [P3 §04 (the 1/sqrt(d) factor);
+                                          P4 §18.2.4 materialised backward]
+A query row with no visible key is defined as O = 0, LSE = -inf and contributes
+no gradient [P3 §04, the all-masked-row convention].
+
+Readings where the pages are loose (each is listed in the design doc):
+  * ``scale`` multiplies Q K^T and is an argument (1/sqrt(d) in every workload);
+    LSE is that of the scaled scores and dQ, dK carry one factor of ``scale``.
+  * LSE uses the natural logarithm.
+  * Causal masking keeps key j for query i iff j <= i, counted within a sequence.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "visible_mask",
+    "head_forward",
+    "head_backward",
+    "forward",
+    "backward",
+    "varlen_forward",
+    "varlen_backward",
+]
+
+
+def visible_mask(rows: np.ndarray, n_keys: int, causal: bool, key_valid=None) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend key j.
+
+    Causal: key j is visible to query i iff j <= i [P4 §18.2.2 item 3, M_ij = 0 for
+    j <= i].  Key padding: invalid keys are hidden from every query [P4 §18.2.2
+    item 4]."""
+    rows = np.asarray(rows)
+    vis = np.ones((len(rows), n_keys), dtype=bool)
+    if causal:
+        vis &= np.arange(n_keys)[None, :] <= rows[:, None]
+    if key_valid is not None:
+        vis &= np.asarray(key_valid, dtype=bool)[None, :]
+    return vis
+
+
+def _scores(q_rows, k, scale, vis):
+    """S = scale * Q K^T with hidden entries set to -inf."""
+    s = scale * (q_rows @ k.T)
+    return np.where(vis, s, -np.inf)
+
+
+def _row_softmax_and_lse(s):
+    """Safe softmax of each row [P2 §3.2]: subtract the row max before exp.
+
+    Returns P (rows with no visible key are all zero) and LSE (-inf for such
+    rows, per the all-masked-row convention of P3 §04)."""
+    m = s.max(axis=1)
+    dead = ~np.isfinite(m)  # every entry -inf
+    m_safe = np.where(dead, 0.0, m)
+    e = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 for hidden keys
+    e[dead] = 0.0
+    denom = e.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(dead[:, None], 0.0, e / np.where(dead, 1.0, denom)[:, None])
+        lse = np.where(dead, -np.inf, m_safe + np.log(np.where(dead, 1.0, denom)))
+    return p, lse
+
+
+def head_forward(q, k, v, scale, causal=False, key_valid=None, rows=None, row_chunk=2048):
+    """O and LSE for one head.  q, k, v: [N, d] (any float dtype, used as fp64).
+
+    ``rows`` selects query rows (default: all), which lets a test check sampled
+    rows of a large problem; each row is still computed from its full score row.
+    Returns (O [len(rows), d] fp64, LSE [len(rows)] fp64)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_keys = k.shape[0]
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    o = np.zeros((len(rows), v.shape[1]))
+    lse = np.zeros(len(rows))
+    for c0 in range(0, len(rows), row_chunk):
+        r = rows[c0:c0 + row_chunk]
+        s = _scores(q[r], k, scale, visible_mask(r, n_keys, causal, key_valid))
+        p, l_ = _row_softmax_and_lse(s)
+        o[c0:c0 + len(r)] = p @ v
+        lse[c0:c0 + len(r)] = l_
+    return o, lse
+
+
+def head_backward(q, k, v, do, scale, causal=False, key_valid=None, row_chunk=2048,
+                  check_d_identity=True):
+    """dQ, dK, dV for one head, plus O, LSE and D (all fp64).
+
+    P is rebuilt from the definition (not from any saved state), then the
+    materialised backward of P4 §18.2.4 / P1 §五 is applied row block by row
+    block: dV and dK are sums over query rows, dQ rows are independent.
+    D is rowsum(dO o O) [P1 §5.2]; when ``check_d_identity`` it is asserted equal
+    to rowsum(P o dP), the form it was derived from."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, n_keys = q.shape[0], k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    o = np.zeros((n, v.shape[1]))
+    lse = np.zeros(n)
+    dvec = np.zeros(n)
+    for c0 in range(0, n, row_chunk):
+        r = np.arange(c0, min(n, c0 + row_chunk))
+        s = _scores(q[r], k, scale, visible_mask(r, n_keys, causal, key_valid))
+        p, l_ = _row_softmax_and_lse(s)
+        o_r = p @ v
+        dp = do[r] @ v.T                      # dP = dO V^T
+        d_r = np.sum(do[r] * o_r, axis=1)     # D = rowsum(dO o O)
+        if check_d_identity:
+            alt = np.sum(p * dp, axis=1)      # D = rowsum(P o dP)
+            tol = 1e-9 * (np.sum(np.abs(do[r]) * np.abs(o_r), axis=1) + np.sum(p * np.abs(dp), axis=1)) + 1e-300
+            if not np.all(np.abs(alt - d_r) <= tol):
+                raise AssertionError("D identity rowsum(dO o O) == rowsum(P o dP) violated")
+        ds = p * (dp - d_r[:, None])          # dS = P o (dP - D)
+        dv += p.T @ do[r]                     # dV = P^T dO
+        dq[r] = scale * (ds @ k)              # dQ = scale dS K
+        dk += scale * (ds.T @ q[r])           # dK = scale dS^T Q
+        o[r] = o_r
+        lse[r] = l_
+        dvec[r] = d_r
+    return dq, dk, dv, o, lse, dvec
+
+
+def forward(q, k, v, scale, causal=False, heads=None):
+    """Dense layout [B, H, N, d].  Returns O [B, H, N, d] and LSE [B, H, N] (fp64).
+
+    ``heads`` optionally restricts the work to a list of (b, h) pairs; the other
+    entries of the outputs are left as NaN."""
+    B, H, N, d = q.shape
+    o = np.full((B, H, N, v.shape[-1]), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
+        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h], v[b, h], scale, causal)
+    return o, lse
+
+
+def backward(q, k, v, do, scale, causal=False, heads=None):
+    """Dense layout [B, H, N, d].  Returns dict with dq, dk, dv, o, lse, D (fp64)."""
+    B, H, N, d = q.shape
+    out = {name: np.full(q.shape, np.nan) for name in ("dq", "dk", "dv", "o")}
+    out["lse"] = np.full((B, H, N), np.nan)
+    out["D"] = np.full((B, H, N), np.nan)
+    for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
+        dq, dk, dv, o, lse, dvec = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+        out["dq"][b, h], out["dk"][b, h], out["dv"][b, h] = dq, dk, dv
+        out["o"][b, h], out["lse"][b, h], out["D"][b, h] = o, lse, dvec
+    return out
+
+
+def _seq_heads(cu_seqlens, H, seqs, heads):
+    seqs = range(len(cu_seqlens) - 1) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    return [(s, h) for s in seqs for h in heads]
+
+
+def varlen_forward(q, k, v, cu_seqlens, scale, causal=False, key_valid=None, seqs=None, heads=None):
+    """Packed layout [T, H, d] with offsets cu_seqlens[nseq+1].  No query attends
+    across a sequence boundary; causal order is the position within the sequence
+    [P4 §18.7.1, variable-length interface].  Returns O [T, H, d], LSE [H, T]."""
+    T, H, d = q.shape
+    o = np.full((T, H, v.shape[-1]), np.nan)
+    lse = np.full((H, T), np.nan)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for s, h in _seq_heads(cu, H, seqs, heads):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b <= a:
+            continue
+        kv = None if key_valid is None else np.asarray(key_valid)[a:b]
+        o[a:b, h], lse[h, a:b] = head_forward(q[a:b, h], k[a:b, h], v[a:b, h], scale, causal, kv)
+    return o, lse
+
+
+def varlen_backward(q, k, v, do, cu_seqlens, scale, causal=False, key_valid=None, seqs=None, heads=None):
+    """Packed layout backward.  Returns dict with dq, dk, dv, o [T, H, d] and lse, D [H, T]."""
+    T, H, d = q.shape
+    out = {name: np.full(q.shape, np.nan) for name in ("dq", "dk", "dv", "o")}
+    out["lse"] = np.full((H, T), np.nan)
+    out["D"] = np.full((H, T), np.nan)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for s, h in _seq_heads(cu, H, seqs, heads):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b <= a:
+            continue
+        kv = None if key_valid is None else np.asarray(key_valid)[a:b]
+        dq, dk, dv, o, lse, dvec = head_backward(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], scale, causal, kv)
+        out["dq"][a:b, h], out["dk"][a:b, h], out["dv"][a:b, h], out["o"][a:b, h] = dq, dk, dv, o
+        out["lse"][h, a:b], out["D"][h, a:b] = lse, dvec
+    return out
