@@ -1,0 +1,29 @@
+"""libmiattn: fused exact attention for AMD MI355X (gfx950).
+
+The compute lives in the HIP library ``libmiattn.so`` (C ABI, declared in
+include/miattn.h); this package is its thin ctypes binding plus the build
+script.  Functions carry the C names and take device tensors:
+
+    attn_fwd, attn_bwd, attn_bwd_workspace_bytes,
+    attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq,
+    attn_fwd_f32, attn_bwd_f32,
+    attn_fwd_varlen, attn_bwd_varlen, attn_bwd_varlen_workspace_bytes
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    MiattnError,
+    attn_bwd,
+    attn_bwd_dkdv,
+    attn_bwd_dq,
+    attn_bwd_f32,
+    attn_bwd_preprocess,
+    attn_bwd_varlen,
+    attn_bwd_varlen_workspace_bytes,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    attn_fwd_f32,
+    attn_fwd_varlen,
+    load,
+    miattn_status_string,
+    miattn_version,
+)

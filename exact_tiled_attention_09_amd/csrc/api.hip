@@ -1,0 +1,227 @@
+// C-ABI layer of libmiattn: argument validation, workspace carving and
+// dispatch to the gfx950 kernels.  Nothing here allocates, frees or
+// synchronises; every launch goes to the caller's stream.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/miattn.h"
+#include "miattn_device.h"
+#include "miattn_launch.h"
+
+using miattn::AttnArgs;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool ptr16(const void* p) { return p != nullptr && aligned(p, 16); }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace: fp32 D (rows entries) then the fp32 dQ accumulator (rows * d).
+size_t workspace_bytes_for(int64_t rows, int d) {
+  return round_up((size_t)rows * sizeof(float), 256) + (size_t)rows * (size_t)d * sizeof(float);
+}
+
+void carve(AttnArgs& a, void* ws, int64_t rows) {
+  a.dvec = static_cast<float*>(ws);
+  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)rows * sizeof(float), 256));
+}
+
+int check_dense(int B, int H, int N, int d, float scale) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || !std::isfinite(scale)) return MIATTN_ERR_INVALID_ARG;
+  // Largest grid: one workgroup per (32-row tile, batch, head).
+  const int64_t tiles = ((int64_t)N + 31) / 32 * (int64_t)B * H;
+  if (tiles > 0x7fffffffLL || (int64_t)B * H * N > (int64_t)1 << 40) return MIATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
+  return MIATTN_OK;
+}
+
+int check_varlen(const int* cu, int nseq, int max_seqlen, int total_tokens, int H, int d, float scale) {
+  if (cu == nullptr || !aligned(cu, 4)) return MIATTN_ERR_INVALID_ARG;
+  if (nseq <= 0 || max_seqlen <= 0 || total_tokens <= 0 || H <= 0 || !std::isfinite(scale))
+    return MIATTN_ERR_INVALID_ARG;
+  const int64_t tiles = ((int64_t)max_seqlen + 31) / 32 * (int64_t)nseq * H;
+  if (tiles > 0x7fffffffLL) return MIATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
+  return MIATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP; }
+
+AttnArgs dense_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                    int N, float scale) {
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = const_cast<void*>(o);
+  a.lse = const_cast<float*>(lse);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.total_tokens = 0;
+  a.scale = scale;
+  a.scale_log2 = scale * miattn::kLog2e;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int miattn_version(void) { return kVersion; }
+
+const char* miattn_status_string(int status) {
+  switch (status) {
+    case MIATTN_OK: return "ok";
+    case MIATTN_ERR_INVALID_ARG: return "invalid argument";
+    case MIATTN_ERR_UNSUPPORTED: return "unsupported head dimension (supported: 64, 128)";
+    case MIATTN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             float scale, int causal, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  return hip_status(miattn::launch_fwd_bf16(a, d, causal != 0, false, stream));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_dense(B, H, N, d, 1.0f) != MIATTN_OK) return 0;
+  return workspace_bytes_for((int64_t)B * H * N, d);
+}
+
+int attn_bwd_preprocess(const void* o, const void* dO, int B, int H, int N, int d, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(o) || !ptr16(dO) || !ptr16(workspace)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, 1.0f)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(nullptr, nullptr, nullptr, o, nullptr, B, H, N, 1.0f);
+  a.dout = dO;
+  carve(a, workspace, rows);
+  return hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream));
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dk, void* dv,
+                  int B, int H, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(lse) || !ptr16(dO) || !ptr16(dk) || !ptr16(dv) ||
+      !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, nullptr, lse, B, H, N, scale);
+  a.dout = dO;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, workspace, rows);
+  return hip_status(miattn::launch_bwd_main_bf16(a, d, causal != 0, false, stream));
+}
+
+int attn_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  if (!ptr16(dq) || !ptr16(workspace)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, N, scale);
+  a.dq = dq;
+  carve(a, workspace, rows);
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, false, stream));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+             void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, workspace, rows);
+  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
+  if (int st = hip_status(miattn::launch_bwd_main_bf16(a, d, causal != 0, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, false, stream));
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+                 float scale, int causal, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  return hip_status(miattn::launch_fwd_f32(a, d, causal != 0, stream));
+}
+
+int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse, const float* dO,
+                 float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, workspace, rows);
+  return hip_status(miattn::launch_bwd_f32(a, d, causal != 0, stream));
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                    int nseq, int max_seqlen, int total_tokens, int H, int d, float scale, int causal,
+                    const unsigned char* key_valid, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_varlen(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, scale)) return st;
+  AttnArgs a = dense_args(q, k, v, o, lse, nseq, H, max_seqlen, scale);
+  a.cu_seqlens = cu_seqlens;
+  a.key_valid = key_valid;
+  a.total_tokens = total_tokens;
+  return hip_status(miattn::launch_fwd_bf16(a, d, causal != 0, true, stream));
+}
+
+size_t attn_bwd_varlen_workspace_bytes(int total_tokens, int H, int d) {
+  if (total_tokens <= 0 || H <= 0 || (d != 64 && d != 128)) return 0;
+  return workspace_bytes_for((int64_t)total_tokens * H, d);
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                    void* dq, void* dk, void* dv, const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens,
+                    int H, int d, float scale, int causal, const unsigned char* key_valid, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_varlen(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, scale)) return st;
+  const int64_t rows = (int64_t)total_tokens * H;
+  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, o, lse, nseq, H, max_seqlen, scale);
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu_seqlens = cu_seqlens;
+  a.key_valid = key_valid;
+  a.total_tokens = total_tokens;
+  carve(a, workspace, rows);
+  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, true, stream))) return st;
+  if (int st = hip_status(miattn::launch_bwd_main_bf16(a, d, causal != 0, true, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, true, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Device-side building blocks shared by the libmiattn kernels (gfx950 / CDNA4).
+//
+// Register layouts used throughout (checked on the device by a lane probe):
+//  * v_mfma_f32_32x32x16_bf16: lane l supplies row (A) or column (B) l % 32 and
+//    eight k-values; lanes 0-31 and 32-63 carry two disjoint k-halves.  A and B
+//    use the same lane/element -> k assignment, so any k order is fine as long
+//    as both operands are packed the same way.
+//  * 32x32 fp32 accumulator: lane l holds column l % 32, register r holds row
+//    (r / 4) * 8 + (l / 32) * 4 + (r % 4).
+//  * ds_read_b64_tr_b16: within each 16-lane group, source lane i names 4
+//    consecutive 16-bit elements M[i][0..3]; result lane j receives
+//    M[j/4 + 4t][j % 4] for t = 0..3.  Pointing source lane i at row (i / 4),
+//    column 4 * (i % 4) of a row-major tile hands result lane j column j of
+//    four consecutive rows: a transposed read of a 4 x 16 block.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MIATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+
+// Everything a kernel needs to address one problem.  Dense tensors are
+// [B, H, N, d] with LSE/D as [B, H, N]; packed tensors are [T, H, d] with
+// LSE/D as [H, T] and per-sequence offsets in cu_seqlens.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;     // D = rowsum(dO * O), laid out like LSE
+  float* dq_acc;   // fp32 dQ accumulator, laid out like Q
+  const int* cu_seqlens;
+  const uint8_t* key_valid;  // per packed token, nonzero = valid key (nullable)
+  int B;           // dense: batch; packed: number of sequences
+  int H;
+  int N;           // dense: sequence length; packed: longest sequence
+  int total_tokens;
+  float scale;     // multiplies Q K^T
+  float scale_log2;  // scale * log2(e)
+};
+
+// Where one (sequence, head) lives.
+struct SeqView {
+  int64_t base;        // element offset of token 0, feature 0
+  int64_t tok_stride;  // elements between consecutive tokens
+  int64_t row_base;    // offset of token 0 in LSE / D
+  int64_t tok0;        // packed index of token 0 (key_valid indexing)
+  int len;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ SeqView seq_view(const AttnArgs& a, int b, int h, int D) {
+  SeqView s;
+  if constexpr (VARLEN) {
+    const int t0 = a.cu_seqlens[b];
+    const int t1 = a.cu_seqlens[b + 1];
+    s.base = ((int64_t)t0 * a.H + h) * D;
+    s.tok_stride = (int64_t)a.H * D;
+    s.row_base = (int64_t)h * a.total_tokens + t0;
+    s.tok0 = t0;
+    s.len = t1 - t0;
+  } else {
+    s.base = ((int64_t)b * a.H + h) * (int64_t)a.N * D;
+    s.tok_stride = D;
+    s.row_base = ((int64_t)b * a.H + h) * (int64_t)a.N;
+    s.tok0 = (int64_t)b * a.N;
+    s.len = a.N;
+  }
+  return s;
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 x) { return __builtin_bit_cast(u32x4, x); }
+
+// Round-to-nearest-even fp32 -> bf16 pairs (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, float x3,
+                                              float x4, float x5, float x6, float x7) {
+  u32x4 u = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3), pack_bf16x2(x4, x5), pack_bf16x2(x6, x7)};
+  return as_bf16x8(u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Transposed 4 x 16 read from a row-major bf16 LDS tile (see the header note).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIATTN_LDS i16x4*)(p));
+  return __builtin_bit_cast(u32x2, t);
+}
+
+__device__ __forceinline__ bf16x8 join_u32x2(u32x2 lo, u32x2 hi) {
+  u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(u);
+}
+
+// Value held by the lane 32 positions away (v_permlane32_swap).
+__device__ __forceinline__ float wave_max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+}  // namespace miattn

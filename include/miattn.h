@@ -1,0 +1,153 @@
+/*
+ * libmiattn -- fused exact attention for AMD MI355X (gfx950), C ABI.
+ *
+ * What it computes, per batch b and head h (or per packed sequence and head):
+ *   S = scale * Q K^T, with masked entries -inf;  P = row-softmax(S);
+ *   O = P V;  LSE_i = ln sum_j exp(S_ij)
+ * ("Attention(Q,K,V) = softmax(QK^T/sqrt(d)) V" in the FlashAttention-1 notes
+ * of BHHXX's Blog, section 1.1, and in "第 18 章 FlashAttention" section
+ * 18.2.1; the log-sum-exp of "解析 FlashAttention（4）：FlashAttention-v2" at
+ * the end of section 三 and in "分块 Attention：重建概率，累计梯度" section 04).
+ * The forward never writes S or P to memory: it keeps the online-softmax
+ * running state (row max m, row sum l, unnormalised output) per query tile
+ * ("解析 FlashAttention（4）" section 四).  The backward rebuilds P from Q, K and
+ * LSE and forms, with upstream gradient dO,
+ *   D = rowsum(dO o O); dP = dO V^T; dS = P o (dP - D);
+ *   dV = P^T dO; dQ = scale dS K; dK = scale dS^T Q
+ * ("解析 FlashAttention（4）" section 五; "分块 Attention" section 04, which
+ * also carries the 1/sqrt(d) factor of dQ and dK).
+ *
+ * Masks: causal keeps key j for query i iff j <= i ("第 18 章" section 18.2.2,
+ * the causal mask M_ij = 0 for j <= i); in the packed interface no query sees
+ * another sequence's keys and positions count from each sequence's start
+ * ("第 18 章" section 18.7.1, the variable-length interface with cumulative
+ * offsets); an optional key-padding mask hides keys from every query
+ * ("第 18 章" section 18.2.2, padding masks).  A query row that sees no key at
+ * all gets O = 0, LSE = -inf and contributes no gradient ("分块 Attention"
+ * section 04, the all-masked-row convention).
+ *
+ * Layouts (row-major, contiguous):
+ *   dense   Q, K, V, O, dO, dQ, dK, dV : [B, H, N, d]     LSE : [B, H, N] fp32
+ *   packed  Q, K, V, O, dO, dQ, dK, dV : [T, H, d]        LSE : [H, T]    fp32
+ *           cu_seqlens : int32 [nseq + 1], cu[0] = 0, non-decreasing,
+ *                        cu[nseq] = T (total_tokens)
+ *           key_valid  : uint8 [T], nonzero = the key may be attended
+ * "bf16" entry points take bfloat16 tensors (raw 16-bit storage); the "_f32"
+ * entry points take fp32 tensors.  LSE and every accumulation are fp32.
+ *
+ * Ownership and streams: every pointer is a device pointer owned by the
+ * caller, including the workspace.  The library allocates nothing, frees
+ * nothing, never synchronises and keeps no global state; all work is queued
+ * on `stream` (0 = the default stream).  Results are valid once the stream
+ * has reached the enqueued work.
+ *
+ * Errors: entry points return MIATTN_OK (0) or a negative status, checked in
+ * this order before anything is launched:
+ *   MIATTN_ERR_INVALID_ARG  a required pointer is NULL or not 16-byte aligned
+ *                           (cu_seqlens: 4-byte), a size is <= 0, scale is
+ *                           not finite, the workspace is too small, or the
+ *                           problem's grid would not fit a launch;
+ *   MIATTN_ERR_UNSUPPORTED  head dim d is not 64 or 128;
+ *   MIATTN_ERR_HIP          a kernel launch was rejected by the runtime.
+ * The contents of cu_seqlens and key_valid live on the device and are not
+ * checked; offsets that break the contract above are undefined behaviour.
+ * Calls that overlap on one stream are ordered; calls on different streams
+ * that share output or workspace buffers race.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIATTN_OK 0
+#define MIATTN_ERR_INVALID_ARG (-1)
+#define MIATTN_ERR_UNSUPPORTED (-2)
+#define MIATTN_ERR_HIP (-3)
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int miattn_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* miattn_status_string(int status);
+
+/* Forward, dense bf16.  q, k, v: [B,H,N,d] bf16 in; o: [B,H,N,d] bf16 out
+ * (round-to-nearest-even); lse: [B,H,N] fp32 out (natural log, -inf for a row
+ * with no visible key).  scale multiplies Q K^T (pass 1/sqrt(d) for the usual
+ * attention); causal != 0 applies the causal mask.  Online-softmax forward of
+ * "解析 FlashAttention（4）：FlashAttention-v2" section 四. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Bytes of device workspace attn_bwd / attn_bwd_f32 need: fp32 D [B,H,N] and
+ * an fp32 dQ accumulator [B,H,N,d].  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward, dense bf16.  Inputs q, k, v, o (from attn_fwd), lse (from
+ * attn_fwd), dO: upstream gradient [B,H,N,d] bf16.  Outputs dq, dk, dv:
+ * [B,H,N,d] bf16 (fp32 accumulation, one final rounding).  workspace: at least
+ * attn_bwd_workspace_bytes(B,H,N,d) bytes, 16-byte aligned, no initial
+ * contents required; it is overwritten.  The LSE receives no gradient.
+ * Equivalent to attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq.
+ * LSE-recompute backward of "解析 FlashAttention（4）" section 五. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv,
+             int B, int H, int N, int d, float scale, int causal,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 1 of attn_bwd: D = rowsum(dO o O) in fp32 into the workspace and a
+ * zeroed dQ accumulator ("解析 FlashAttention（4）" section 5.2). */
+int attn_bwd_preprocess(const void* o, const void* dO, int B, int H, int N, int d,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 2 of attn_bwd: one pass over key tiles that writes dk and dv and adds
+ * every query tile's dQ contribution into the workspace accumulator
+ * ("解析 FlashAttention（4）" section 5.4).  Needs stage 1 on the same workspace. */
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                  void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 3 of attn_bwd: dq = bf16(scale * accumulator). */
+int attn_bwd_dq(void* dq, int B, int H, int N, int d, float scale,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fp32 forward: same contract as attn_fwd with fp32 q, k, v, o. */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* fp32 backward: same contract as attn_bwd with fp32 tensors; workspace size
+ * from attn_bwd_workspace_bytes. */
+int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                 const float* dO, float* dq, float* dk, float* dv,
+                 int B, int H, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward over packed variable-length sequences, bf16.  q, k, v, o: [T,H,d];
+ * lse: [H,T] fp32.  cu_seqlens: device int32 [nseq+1]; max_seqlen: the
+ * longest sequence (rows past it are not computed); total_tokens: T.
+ * key_valid: device uint8 [T] or NULL (all keys valid). */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens,
+                    int H, int d, float scale, int causal, const unsigned char* key_valid,
+                    hipStream_t stream);
+
+/* Workspace bytes for attn_bwd_varlen: fp32 D [H,T] and dQ accumulator [T,H,d]. */
+size_t attn_bwd_varlen_workspace_bytes(int total_tokens, int H, int d);
+
+/* Backward over packed variable-length sequences, bf16; arguments as in
+ * attn_fwd_varlen plus those of attn_bwd. */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens,
+                    int H, int d, float scale, int causal, const unsigned char* key_valid,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

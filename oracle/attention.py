@@ -32,6 +32,7 @@ __all__ = [
     "visible_mask",
     "head_forward",
     "head_backward",
+    "head_backward_sampled",
     "forward",
     "backward",
     "varlen_forward",
@@ -138,6 +139,48 @@ def head_backward(q, k, v, do, scale, causal=False, key_valid=None, row_chunk=20
         o[r] = o_r
         lse[r] = l_
         dvec[r] = d_r
+    return dq, dk, dv, o, lse, dvec
+
+
+def head_backward_sampled(q, k, v, do, scale, causal=False, key_valid=None, query_rows=(), key_cols=(),
+                          row_chunk=2048):
+    """The backward of one head evaluated only at chosen outputs: dQ at
+    ``query_rows`` and dK, dV at ``key_cols`` (plus O, LSE and D for all rows).
+
+    Same definition as ``head_backward``: dQ_i = scale sum_j dS_ij K_j needs
+    row i of P and dP; dV_j = sum_i P_ij dO_i and dK_j = scale sum_i dS_ij Q_i
+    need column j of P and dS, i.e. LSE and D of every row.  Lets a test check
+    a problem too large to materialise whole on the CPU."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, n_keys = q.shape[0], k.shape[0]
+    o, lse = head_forward(q, k, v, scale, causal, key_valid, row_chunk=row_chunk)
+    dvec = np.sum(do * o, axis=1)
+    rows = np.asarray(query_rows, dtype=np.int64)
+    cols = np.asarray(key_cols, dtype=np.int64)
+    dq = np.zeros((len(rows), q.shape[1]))
+    if len(rows):
+        s = _scores(q[rows], k, scale, visible_mask(rows, n_keys, causal, key_valid))
+        dead = ~np.isfinite(lse[rows])
+        p = np.where(dead[:, None], 0.0, np.exp(s - np.where(dead, 0.0, lse[rows])[:, None]))
+        dp = do[rows] @ v.T
+        ds = p * (dp - dvec[rows][:, None])
+        dq = scale * (ds @ k)
+    dk = np.zeros((len(cols), k.shape[1]))
+    dv = np.zeros((len(cols), v.shape[1]))
+    if len(cols):
+        for c0 in range(0, n, row_chunk):
+            r = np.arange(c0, min(n, c0 + row_chunk))
+            vis = visible_mask(r, n_keys, causal, key_valid)[:, cols]
+            s = np.where(vis, scale * (q[r] @ k[cols].T), -np.inf)
+            dead = ~np.isfinite(lse[r])
+            p = np.where(dead[:, None], 0.0, np.exp(s - np.where(dead, 0.0, lse[r])[:, None]))
+            dp = do[r] @ v[cols].T
+            ds = p * (dp - dvec[r][:, None])
+            dv += p.T @ do[r]
+            dk += scale * (ds.T @ q[r])
     return dq, dk, dv, o, lse, dvec
 
 

@@ -1,0 +1,83 @@
+"""Shared helpers for the GPU parity tests: device copies of the seeded inputs,
+error metrics and the tolerance bar (not a test module).
+
+Tolerances (fixed here, used by every parity test):
+  fp32 path:  max |GPU - oracle| <= 1e-5 on O, LSE, dQ, dK, dV.
+  bf16 path:  O: max abs <= 2e-2; O, dQ, dK, dV: relative Frobenius error
+              <= 1e-2; LSE: max abs <= 1e-3.  The oracle runs in fp64 on the
+              identical bf16-rounded inputs.  Rows whose LSE is -inf must be
+              -inf on both sides with O exactly zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32_MAX_ABS = 1e-5
+BF16_O_MAX_ABS = 2e-2
+BF16_REL_FRO = 1e-2
+LSE_MAX_ABS = 1e-3
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    """float32 numpy (values exact in dtype) -> contiguous device tensor."""
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return t.cuda().contiguous()
+
+
+def to_np(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def max_abs(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def rel_fro(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = float(np.linalg.norm(b))
+    num = float(np.linalg.norm(a - b))
+    if den == 0.0:
+        return num
+    return num / den
+
+
+def check_lse(gpu_lse, ref_lse, tol=LSE_MAX_ABS, what="LSE"):
+    g = np.asarray(gpu_lse, np.float64)
+    r = np.asarray(ref_lse, np.float64)
+    dead_r = np.isneginf(r)
+    dead_g = np.isneginf(g)
+    assert np.array_equal(dead_r, dead_g), f"{what}: -inf rows differ ({dead_r.sum()} oracle vs {dead_g.sum()} GPU)"
+    assert np.all(np.isfinite(g[~dead_g])), f"{what}: non-finite values"
+    err = max_abs(g[~dead_r], r[~dead_r])
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+    return err
+
+
+def check_bf16(gpu, ref, what, max_abs_tol=None):
+    err_fro = rel_fro(gpu, ref)
+    err_abs = max_abs(gpu, ref)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    assert err_fro <= BF16_REL_FRO, f"{what}: relative Frobenius error {err_fro:.3e} > {BF16_REL_FRO:.0e}"
+    if max_abs_tol is not None:
+        assert err_abs <= max_abs_tol, f"{what}: max abs error {err_abs:.3e} > {max_abs_tol:.0e}"
+    return err_fro, err_abs
+
+
+def check_f32(gpu, ref, what, tol=F32_MAX_ABS):
+    err = max_abs(gpu, ref)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.0e}"
+    return err

@@ -1,0 +1,108 @@
+"""The C-ABI library loads on the CPU and exports every symbol the header
+declares; host-side validation rejects bad arguments before any launch.
+CPU only: nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+LIB = os.path.join(ROOT, "exact_tiled_attention_09_amd", "libmiattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmiattn.so not built")
+
+
+def _declared():
+    with open(HEADER) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for need in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32",
+                 "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
+                 "miattn_status_string"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_binding_signatures_cover_the_header():
+    from exact_tiled_attention_09_amd import _lib
+    assert sorted(_lib.SIGNATURES) == _declared()
+    _lib.load()
+
+
+def _lib():
+    from exact_tiled_attention_09_amd import _lib as L
+    return L.load()
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.miattn_version() >= 100
+    assert lib.miattn_status_string(0) == b"ok"
+    assert b"invalid" in lib.miattn_status_string(-1)
+    assert b"unsupported" in lib.miattn_status_string(-2)
+
+
+def test_workspace_sizes():
+    lib = _lib()
+    B, H, N, d = 4, 32, 4096, 128
+    rows = B * H * N
+    want = (rows * 4 + 255) // 256 * 256 + rows * d * 4
+    assert lib.attn_bwd_workspace_bytes(B, H, N, d) == want
+    assert lib.attn_bwd_workspace_bytes(B, H, N, 96) == 0
+    assert lib.attn_bwd_workspace_bytes(0, H, N, d) == 0
+    assert lib.attn_bwd_varlen_workspace_bytes(1000, 32, 64) == (32000 * 4 + 255) // 256 * 256 + 32000 * 64 * 4
+
+
+# A fake, aligned, non-null "device" address: validation fails before it is used.
+FAKE = ctypes.c_void_p(1 << 20)
+NULL = ctypes.c_void_p(0)
+MIS = ctypes.c_void_p((1 << 20) + 2)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(q=NULL), -1),
+    (dict(o=MIS), -1),
+    (dict(B=0), -1),
+    (dict(N=-5), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(d=96), -2),
+    (dict(d=256), -2),
+])
+def test_forward_argument_validation(case, expect):
+    lib = _lib()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, scale=0.125)
+    args.update(case)
+    st = lib.attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"], args["N"],
+                      args["d"], args["scale"], 0, NULL)
+    assert st == expect
+
+
+def test_backward_rejects_small_workspace():
+    lib = _lib()
+    need = lib.attn_bwd_workspace_bytes(1, 2, 64, 64)
+    st = lib.attn_bwd(*([FAKE] * 9), 1, 2, 64, 64, 0.125, 1, FAKE, need - 4, NULL)
+    assert st == -1
+    st = lib.attn_bwd_f32(*([FAKE] * 9), 1, 2, 64, 64, 0.125, 1, FAKE, need - 4, NULL)
+    assert st == -1
+
+
+def test_varlen_validation():
+    lib = _lib()
+    base = [FAKE] * 5
+    assert lib.attn_fwd_varlen(*base, NULL, 2, 10, 15, 2, 64, 0.1, 1, NULL, NULL) == -1
+    assert lib.attn_fwd_varlen(*base, FAKE, 0, 10, 15, 2, 64, 0.1, 1, NULL, NULL) == -1
+    assert lib.attn_fwd_varlen(*base, FAKE, 2, 10, 15, 2, 80, 0.1, 1, NULL, NULL) == -2
+    assert lib.attn_fwd_varlen(*base, ctypes.c_void_p((1 << 20) + 2), 2, 10, 15, 2, 64, 0.1, 1, NULL, NULL) == -1

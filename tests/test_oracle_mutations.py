@@ -15,7 +15,7 @@ def _mutant(module_file, old, new, name):
     path = os.path.join(ROOT, "oracle", module_file)
     with open(path) as f:
         src = f.read()
-    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     mod = types.ModuleType(name)
     mod.__package__ = "oracle"
     mod.__file__ = path

@@ -370,3 +370,21 @@ def test_varlen_sequences_do_not_interact():
     out2 = A.varlen_backward(q, k2, v, g, cu, 0.5, causal=True)
     np.testing.assert_array_equal(out2["o"][:cu[2]], out["o"][:cu[2]])
     np.testing.assert_array_equal(out2["dq"][cu[3]:], out["dq"][cu[3]:])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_matches_full_backward(causal):
+    """The sampled form picks the same entries out of the full backward."""
+    rng = np.random.default_rng(12)
+    n, d = 45, 6
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    kv = np.ones(n, np.uint8)
+    kv[[0, 7, 30]] = 0
+    rows = [0, 3, 7, 44]
+    cols = [0, 1, 30, 44]
+    dq, dk, dv, o, lse, dvec = A.head_backward(q, k, v, g, 0.4, causal, kv, row_chunk=8)
+    sq, sk, sv_, so, sl, sd = A.head_backward_sampled(q, k, v, g, 0.4, causal, kv, rows, cols, row_chunk=16)
+    np.testing.assert_allclose(sq, dq[rows], atol=1e-13)
+    np.testing.assert_allclose(sk, dk[cols], atol=1e-13)
+    np.testing.assert_allclose(sv_, dv[cols], atol=1e-13)
+    np.testing.assert_allclose(so, o, atol=1e-14)
