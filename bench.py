@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark: fused exact attention forward + backward on one MI355X.
+
+One step is one full pass of the hot path over the workload: the forward
+(attn_fwd) followed by the whole backward (D pre-pass, key-tile pass with dQ
+accumulation, dQ finalize: the three stages attn_bwd runs).  Inputs are
+seeded synthetic tensors already resident in HBM before the timed region.
+
+Workload (default): causal self-attention, B=4, H=32, N=4096, d=128, bf16,
+scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) rounded to bf16, seed 0.
+
+FLOP accounting: forward 4*B*H*N^2*d, halved under the causal mask; backward
+2.5x the forward (five N^2*d products, the recompute of S included).
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (256 CUs at 2.4 GHz).
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4e9 clk/s x 4096 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {
+    "causal_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128, causal=True, sigma_qk=1.0),
+    "causal_b1_h16_n16384_d128": dict(B=1, H=16, N=16384, d=128, causal=True, sigma_qk=1.5),
+    "noncausal_b8_h16_n2048_d64": dict(B=8, H=16, N=2048, d=64, causal=False, sigma_qk=1.0),
+}
+DEFAULT = "causal_b4_h32_n4096_d128"
+METRIC = "attn fwd/bwd TFLOPS + % MFMA bf16 peak, causal B4 H32 N4096 d128, 1 MI355X"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def flops(B, H, N, d, causal):
+    fwd = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+    return fwd, 2.5 * fwd
+
+
+def cpu_baseline(inp, cfg, scale):
+    """The fp64 oracle on one (b, h) head, forward + backward, scaled to the
+    whole batch (B*H heads): a reported baseline, not a target."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as A
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    A.head_backward(inp["q"][0, 0], inp["k"][0, 0], inp["v"][0, 0], inp["do"][0, 0], scale, cfg["causal"])
+    dt = time.perf_counter() - t0
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    f_fwd, f_bwd = flops(1, 1, N, d, cfg["causal"])
+    return {
+        "value": round((f_fwd + f_bwd) / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"one head (b=0, h=0) of the workload, forward+backward, {dt:.2f} s; "
+                  f"whole-job time scales by B*H = {B * H}: {dt * B * H:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every box here has a single MI355X "
+              "and this build has no multi-GPU path", file=sys.stderr)
+        return 2
+    if args.steps <= 0 or args.warmup < 0:
+        print("--steps must be > 0 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import exact_tiled_attention_09_amd as M
+    from attn_inputs import dense_inputs
+    M.load()
+
+    cfg = WORKLOADS[args.workload]
+    B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
+    scale = 1.0 / math.sqrt(d)
+    log(f"workload {args.workload}: generating inputs")
+    inp = dense_inputs(B, H, N, d, "bf16", seed=0, sigma_qk=cfg["sigma_qk"])
+    dev = {n: torch.from_numpy(inp[n]).to(torch.bfloat16).cuda().contiguous() for n in ("q", "k", "v", "do")}
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(M.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.attn_fwd(q, k, v, o, lse, scale, causal, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.attn_bwd_preprocess(o, do, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        M.attn_bwd_dkdv(q, k, v, lse, do, dk, dv, scale, causal, ws, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        M.attn_bwd_dq(dq, scale, ws, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {"fwd": [], "bwd_prep": [], "bwd_main": [], "bwd_dq": [], "step": []}
+    for ev in events:
+        per["fwd"].append(ev[0].elapsed_time(ev[1]))
+        per["bwd_prep"].append(ev[1].elapsed_time(ev[2]))
+        per["bwd_main"].append(ev[2].elapsed_time(ev[3]))
+        per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
+        per["step"].append(ev[0].elapsed_time(ev[4]))
+    mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
+    med = {k_: statistics.median(v_) for k_, v_ in per.items()}
+
+    f_fwd, f_bwd = flops(B, H, N, d, causal)
+    ms_step = wall * 1e3 / args.steps
+    bwd_ms = mean["bwd_prep"] + mean["bwd_main"] + mean["bwd_dq"]
+    tflops_fwd = f_fwd / (mean["fwd"] * 1e-3) / 1e12
+    tflops_bwd = f_bwd / (bwd_ms * 1e-3) / 1e12
+    tflops_main = f_bwd / (mean["bwd_main"] * 1e-3) / 1e12
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+
+    elem = B * H * N * d
+    rows = B * H * N
+    prep_bytes = 2 * elem * 2 + rows * 4 + elem * 4       # read O, dO; write D; zero the dQ accumulator
+    dq_bytes = elem * 4 + elem * 2                         # read fp32 accumulator, write bf16 dQ
+    fwd_bytes = 3 * elem * 2 + elem * 2 + rows * 4         # read Q, K, V; write O, LSE
+
+    result = {
+        "metric": METRIC if args.workload == DEFAULT else f"attn fwd+bwd TFLOPS, {args.workload}, 1 MI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"exact attention fwd+bwd, {'causal' if causal else 'non-causal'} "
+                               f"B{B} H{H} N{N} d{d} bf16", "B": B, "H": H, "N": N, "d": d,
+                   "causal": causal, "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd},
+        "fwd": {"ms": round(mean["fwd"], 4), "ms_median": round(med["fwd"], 4), "tflops": round(tflops_fwd, 2),
+                "pct_mfma_peak": round(100 * tflops_fwd / PEAK_BF16_TFLOPS, 2),
+                "gbps": round(fwd_bytes / (mean["fwd"] * 1e-3) / 1e9, 1)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
+                "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2),
+                "main_ms": round(mean["bwd_main"], 4),
+                "prep_ms": round(mean["bwd_prep"], 4),
+                "prep_gbps": round(prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9, 1),
+                "prep_pct_hbm_peak": round(100 * prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                "dq_ms": round(mean["bwd_dq"], 4),
+                "dq_gbps": round(dq_bytes / (mean["bwd_dq"] * 1e-3) / 1e9, 1),
+                "dq_pct_hbm_peak": round(100 * dq_bytes / (mean["bwd_dq"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)},
+        "roofline": {"kernel": "bwd_main_kernel (attn_bwd_dkdv)", "bound": "mfma",
+                     "achieved": round(tflops_main, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops_main / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": f_bwd, "avg_launch_ms": round(mean["bwd_main"], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one head")
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, scale)
+    del np
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

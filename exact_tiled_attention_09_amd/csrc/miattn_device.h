@@ -127,18 +127,17 @@ __device__ __forceinline__ bf16x8 join_u32x2(u32x2 lo, u32x2 hi) {
   return as_bf16x8(u);
 }
 
-// Value held by the lane 32 positions away (v_permlane32_swap).
-__device__ __forceinline__ float wave_max_halves(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+// Value held by the lane 32 positions away, through the LDS crossbar
+// (ds_bpermute_b32; no LDS memory is touched).  v_permlane32_swap would be
+// the natural instruction, but the compiler in use folds its two results into
+// one register when both operands carry the same value, so it is not used.
+__device__ __forceinline__ float lane_xor32(float x) {
+  const int addr = (int)((__lane_id() ^ 32u) << 2);
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
 }
 
-__device__ __forceinline__ float wave_sum_halves(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
-}
+__device__ __forceinline__ float wave_max_halves(float x) { return fmaxf(x, lane_xor32(x)); }
+__device__ __forceinline__ float wave_sum_halves(float x) { return x + lane_xor32(x); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

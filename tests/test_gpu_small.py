@@ -44,13 +44,19 @@ def _run_dense(lib, inp, scale, causal, dtype, bwd=True):
     return {k_: to_np(v_) for k_, v_ in out.items()}
 
 
-def _check(out, ref, dtype):
+def _check(out, ref, dtype, f32_relative=False):
+    """f32: max abs <= 1e-5; with ``f32_relative`` the bar is 1e-5 times the
+    largest reference magnitude (when above 1), for inputs scaled well past
+    unit variance where fp32 rounding alone exceeds 1e-5."""
     if dtype == "f32":
-        check_f32(out["o"], ref["o"], "O")
-        check_lse(out["lse"], ref["lse"], tol=1e-5)
+        def tol(r):
+            return 1e-5 * (max(1.0, float(np.max(np.abs(r)))) if f32_relative else 1.0)
+        check_f32(out["o"], ref["o"], "O", tol(ref["o"]))
+        fin = np.isfinite(ref["lse"])
+        check_lse(out["lse"], ref["lse"], tol=tol(ref["lse"][fin]))
         for g in ("dq", "dk", "dv"):
             if g in out:
-                check_f32(out[g], ref[g], g)
+                check_f32(out[g], ref[g], g, tol(ref[g]))
     else:
         check_bf16(out["o"], ref["o"], "O", max_abs_tol=BF16_O_MAX_ABS)
         check_lse(out["lse"], ref["lse"])
@@ -101,7 +107,7 @@ def test_scale_edge_cases(lib, dtype, scale):
     inp = dense_inputs(1, 2, 150, 64, dtype, seed=5, sigma_qk=2.0)
     out = _run_dense(lib, inp, scale, True, dtype)
     ref = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True)
-    _check(out, ref, dtype)
+    _check(out, ref, dtype, f32_relative=True)
 
 
 def _run_varlen(lib, inp, scale, causal, key_valid=None, bwd=True):
