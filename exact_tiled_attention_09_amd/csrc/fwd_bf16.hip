@@ -11,14 +11,18 @@
 //    softmax traffic).
 //  * the wave computes S^T = K Q^T so that the 32x32 accumulator puts one query
 //    per lane column: row max / row sum are in-lane over 16 registers plus one
-//    permlane32 swap, and the rescale factor is a per-lane scalar.
+//    exchange with the lane 32 away, and the rescale factor is a per-lane
+//    scalar.
 //  * P^T leaves the accumulator already in the B-operand layout of
 //    O^T += V^T P^T; V^T comes from the row-major V tile through the LDS
 //    transpose read, so neither P nor V is shuffled.
 //  * K/V tiles of BC = 64 keys are double-buffered in LDS (one barrier per
 //    tile); Q stays in registers for the whole key loop.
-//  * softmax runs in base 2 with scale * log2(e) folded into one FMA; the
-//    accumulator is rescaled only when some row's max moved.
+//  * softmax runs in base 2 with scale * log2(e) folded into one FMA.  A row's
+//    reference max is only raised when a tile's max exceeds it by more than
+//    kLazyMax (base-2 units); below that the stale reference is kept, P~ stays
+//    below 2^kLazyMax, and O~ and l need no rescale.  Any reference value gives
+//    the same O = O~ / l and LSE = m + log2 l, so this changes only rounding.
 //  * causal: key tiles above the diagonal are never loaded; only tiles that
 //    cross the diagonal, the sequence end or a padded key are masked
 //    element-wise; query tiles are issued heaviest first; consecutive
@@ -27,10 +31,14 @@
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
+#include <cstdlib>
+
 namespace miattn {
 
-template <int D, int QB, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
+constexpr float kLazyMax = 8.0f;
+
+template <int D, int QB, int NW, int MINB, bool CAUSAL, bool VARLEN, bool KPAD>
+__global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
   constexpr int BC = 64;                 // keys per tile
   constexpr int BR = NW * QB * 32;       // query rows per workgroup
   constexpr int KS = D / 16;             // k-steps of S over the head dim
@@ -212,7 +220,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(AttnArgs a, int n_
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
         mx = wave_max_halves(mx);
         const float mt = need_mask ? mx : mx * c;
-        const float m_new = fmaxf(m[qb], mt);
+        const float m_new = (mt > m[qb] + kLazyMax) ? mt : m[qb];
         const bool dead = m_new == kNegInf;  // no visible key yet for this row
         const float alpha = dead ? 1.f : fast_exp2(m[qb] - m_new);
         const float mu = dead ? 0.f : m_new;
@@ -285,34 +293,54 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(AttnArgs a, int n_
   }
 }
 
-template <int D, int QB, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
+template <int D, int QB, int NW, int MINB, bool CAUSAL, bool VARLEN, bool KPAD>
 static hipError_t launch_fwd_bf16_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BR = NW * QB * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, MINB, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, stream, a, n_qtiles);
   return hipGetLastError();
 }
 
-template <int D, int QB, int NW>
+template <int D, int QB, int NW, int MINB>
 static hipError_t dispatch_fwd(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
   if (varlen) {
-    if (causal) return kpad ? launch_fwd_bf16_t<D, QB, NW, true, true, true>(a, s)
-                            : launch_fwd_bf16_t<D, QB, NW, true, true, false>(a, s);
-    return kpad ? launch_fwd_bf16_t<D, QB, NW, false, true, true>(a, s)
-                : launch_fwd_bf16_t<D, QB, NW, false, true, false>(a, s);
+    if (causal) return kpad ? launch_fwd_bf16_t<D, QB, NW, MINB, true, true, true>(a, s)
+                            : launch_fwd_bf16_t<D, QB, NW, MINB, true, true, false>(a, s);
+    return kpad ? launch_fwd_bf16_t<D, QB, NW, MINB, false, true, true>(a, s)
+                : launch_fwd_bf16_t<D, QB, NW, MINB, false, true, false>(a, s);
   }
-  return causal ? launch_fwd_bf16_t<D, QB, NW, true, false, false>(a, s)
-                : launch_fwd_bf16_t<D, QB, NW, false, false, false>(a, s);
+  return causal ? launch_fwd_bf16_t<D, QB, NW, MINB, true, false, false>(a, s)
+                : launch_fwd_bf16_t<D, QB, NW, MINB, false, false, false>(a, s);
+}
+
+// Tile shapes: (query blocks per wave, waves per workgroup, workgroups per CU).
+// MIATTN_FWD_TILE=<n> picks a shape for tuning sweeps; the default is the
+// measured best.
+static int fwd_tile_choice() {
+  static int choice = [] {
+    const char* e = getenv("MIATTN_FWD_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  return choice;
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream) {
   const bool kpad = varlen && a.key_valid != nullptr;
-  if (d == 128) return dispatch_fwd<128, 2, 4>(a, causal, varlen, kpad, stream);
-  if (d == 64) return dispatch_fwd<64, 2, 4>(a, causal, varlen, kpad, stream);
+  const int t = fwd_tile_choice();
+  if (d == 128) {
+    if (t == 1) return dispatch_fwd<128, 2, 4, 1>(a, causal, varlen, kpad, stream);
+    if (t == 2) return dispatch_fwd<128, 1, 4, 2>(a, causal, varlen, kpad, stream);
+    return dispatch_fwd<128, 1, 8, 1>(a, causal, varlen, kpad, stream);
+  }
+  if (d == 64) {
+    if (t == 1) return dispatch_fwd<64, 2, 4, 1>(a, causal, varlen, kpad, stream);
+    if (t == 2) return dispatch_fwd<64, 1, 4, 2>(a, causal, varlen, kpad, stream);
+    return dispatch_fwd<64, 1, 8, 1>(a, causal, varlen, kpad, stream);
+  }
   return hipErrorInvalidValue;
 }
 
