@@ -38,6 +38,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Extra flags per source.  The backward kernel keeps its dK/dV accumulators
+# live across the query-tile loop; in AGPR form the compiler copies them
+# between register files every iteration, the VGPR form does not.
+FILE_FLAGS = {
+    "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -47,7 +55,7 @@ def hipcc() -> str:
 
 def _compile(src: str, obj: str, verbose: bool) -> tuple[str, float]:
     t0 = time.time()
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

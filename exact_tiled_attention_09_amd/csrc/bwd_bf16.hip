@@ -9,8 +9,8 @@
 // Three kernels, all on the caller's stream:
 //  1. bwd_prep: D for every row (fp32) and a zeroed fp32 dQ accumulator.
 //  2. bwd_main: one workgroup per (sequence, head, 128-key tile); each of the
-//     4 waves owns 32 keys with their dK/dV accumulators in registers and K, V
-//     as resident MFMA operands.  For every 64-row query tile at or after the
+//     4 waves owns 32 keys with their dK/dV accumulators in registers; the
+//     workgroup's K and V stay in LDS as MFMA operands.  For every 64-row query tile at or after the
 //     diagonal it recomputes S = Q K^T, P, dP = dO V^T and dS, accumulates
 //     dV += P^T dO and dK += dS^T Q (P/dS come straight out of the accumulator
 //     in A-operand layout; dO and Q are fed through the LDS transpose read),
@@ -61,6 +61,11 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows)
 }
 
 // ---------------------------------------------------------------- kernel 2
+// LDS holds the workgroup's K and V tiles for its whole life (row-major, read
+// as MFMA operands), one Q / dO tile (refilled while the dQ product runs: the
+// barrier before that product is the last point any wave reads them), and the
+// dS^T tile.  Per wave, registers hold only the dK/dV accumulators and the
+// S/dP tiles, so everything fits the 256 architectural VGPRs.
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
 __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktiles) {
   constexpr int NW = 4;
@@ -68,7 +73,7 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
   constexpr int BQ = 64;             // query rows per step
   constexpr int KS = D / 16;         // k-steps over the head dim
   constexpr int DB = D / 32;
-  constexpr int ROW = D + 16;        // padded bf16 row of Q / dO / K tiles
+  constexpr int ROW = D + 16;        // padded bf16 row of Q / dO / K / V tiles
   constexpr int SROW = BQ + 16;      // padded bf16 row of the dS^T tile
   constexpr int CH_PER_ROW = D / 8;
   constexpr int QCPT = BQ * CH_PER_ROW / 256;  // 16-byte chunks per thread, Q tile
@@ -77,11 +82,12 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
   static_assert(DQ_UNITS % NW == 0, "dQ units must split evenly over the waves");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[BK * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BQ * ROW];   // dO
-  __shared__ __attribute__((aligned(16))) uint16_t sDS[BK * SROW];    // dS^T, bf16
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];            // LSE * log2(e), +inf if dead
-  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];           // D
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BK * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[BQ * ROW];    // dO
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[BK * SROW];  // dS^T, bf16
+  __shared__ __attribute__((aligned(16))) float sL[BQ];             // LSE * log2(e), +inf if dead
+  __shared__ __attribute__((aligned(16))) float sDv[BQ];            // D
 
   const int nbh = a.B * a.H;
   const int bh = blockIdx.x % nbh;
@@ -106,36 +112,28 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
   const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
   const uint16_t* __restrict__ gp = (const uint16_t*)a.dout + sv.base;
 
-  // This wave's keys as B operands (lane = key column, 8 features per k-step).
-  const int wk0 = k0 + wave * 32;
+  const int wk0 = k0 + wave * 32;  // this wave's 32 keys
   const int my_key = wk0 + l32;
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-    if (my_key < len) {
-      xk = *(const u32x4*)(kp + (int64_t)my_key * sv.tok_stride + ks * 16 + hi * 8);
-      xv = *(const u32x4*)(vp + (int64_t)my_key * sv.tok_stride + ks * 16 + hi * 8);
-    }
-    kf[ks] = as_bf16x8(xk);
-    vf[ks] = as_bf16x8(xv);
-  }
   bool key_ok = my_key < len;
   if constexpr (KPAD) {
     if (key_ok) key_ok = a.key_valid[sv.tok0 + my_key] != 0;
   }
   const bool any_bad_key = wave_any(!key_ok);
 
-  // The workgroup's K tile, row-major, for the dQ product.
+  // The workgroup's K and V tiles, row-major (rows past the sequence are zero).
 #pragma unroll
   for (int cidx = 0; cidx < KCPT; ++cidx) {
     const int chunk = tid + cidx * 256;
     const int row = chunk / CH_PER_ROW;
     const int col = (chunk - row * CH_PER_ROW) * 8;
     const int key = k0 + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < len) x = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
-    *(u32x4*)(sK + row * ROW + col) = x;
+    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+    if (key < len) {
+      xk = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
+      xv = *(const u32x4*)(vp + (int64_t)key * sv.tok_stride + col);
+    }
+    *(u32x4*)(sK + row * ROW + col) = xk;
+    *(u32x4*)(sV + row * ROW + col) = xv;
   }
 
   f32x16 dk[DB], dv[DB];
@@ -177,112 +175,98 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&]() {
 #pragma unroll
     for (int cidx = 0; cidx < QCPT; ++cidx) {
       const int chunk = tid + cidx * 256;
       const int row = chunk / CH_PER_ROW;
       const int col = (chunk - row * CH_PER_ROW) * 8;
-      *(u32x4*)(&sQ[buf][row * ROW + col]) = rq[cidx];
-      *(u32x4*)(&sG[buf][row * ROW + col]) = rg[cidx];
+      *(u32x4*)(&sQ[row * ROW + col]) = rq[cidx];
+      *(u32x4*)(&sG[row * ROW + col]) = rg[cidx];
     }
     if (tid < BQ) {
-      sL[buf][tid] = rl;
-      sDv[buf][tid] = rd;
+      sL[tid] = rl;
+      sDv[tid] = rd;
     }
   };
 
   if (qt_begin < n_qt) {
     load_tile(qt_begin);
-    store_tile(0);
+    store_tile();
   }
   __syncthreads();
 
   // Transpose-read addressing shared by every "rows of 4 x 16" operand.
   const int tr_row = hi * 4 + ((lane >> 2) & 3);
   const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  // B operands of S = Q K^T and dP = dO V^T: lane = this wave's key, 8 features.
+  const uint16_t* kb_row = sK + (wave * 32 + l32) * ROW + hi * 8;
+  const uint16_t* vb_row = sV + (wave * 32 + l32) * ROW + hi * 8;
 
   for (int it = qt_begin; it < n_qt; ++it) {
-    const int buf = (it - qt_begin) & 1;
     const int q0 = it * BQ;
     if (it + 1 < n_qt) load_tile(it + 1);
 
     const bool live = !CAUSAL || (q0 + BQ - 1 >= wk0);
     if (live) {
-      const uint16_t* q_s = sQ[buf];
-      const uint16_t* g_s = sG[buf];
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int off = (qb * 32 + l32) * ROW + ks * 16 + hi * 8;
-          s[qb] = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), kf[ks], s[qb]);
-          dp[qb] = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), vf[ks], dp[qb]);
-        }
-      }
-
       bool need_mask = (wk0 + 31 >= len) || any_bad_key;
       if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0);
+      // One 32-row half of the query tile at a time keeps S and dP to 32
+      // registers; the scheduling barriers stop the halves from interleaving.
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = (qb * 32 + l32) * ROW + ks * 16 + hi * 8;
+          s = mfma_bf16(as_bf16x8(*(const u32x4*)(sQ + off)), as_bf16x8(*(const u32x4*)(kb_row + ks * 16)), s);
+          dp = mfma_bf16(as_bf16x8(*(const u32x4*)(sG + off)), as_bf16x8(*(const u32x4*)(vb_row + ks * 16)), dp);
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + g * 8 + hi * 4;
-          const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
-          const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
+          const f32x4 lv = *(const f32x4*)(&sL[ql]);
+          const f32x4 dvv = *(const f32x4*)(&sDv[ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = g * 4 + e;
-            float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -lv[e]));
+            float p = fast_exp2(__builtin_fmaf(s[r], c, -lv[e]));
             if (need_mask) {
               bool vis = key_ok;
               if (CAUSAL) vis = vis && (my_key <= q0 + ql + e);
               p = vis ? p : 0.f;
             }
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - dvv[e]);
+            s[r] = p;
+            dp[r] = p * (dp[r] - dvv[e]);
           }
         }
-      }
-
-      // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA.
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA.
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const f32x16& ps = s[qb];
-          const f32x16& dss = dp[qb];
-          const bf16x8 pa = pack_bf16x8(ps[8 * t + 0], ps[8 * t + 1], ps[8 * t + 2], ps[8 * t + 3],
-                                        ps[8 * t + 4], ps[8 * t + 5], ps[8 * t + 6], ps[8 * t + 7]);
-          const bf16x8 da = pack_bf16x8(dss[8 * t + 0], dss[8 * t + 1], dss[8 * t + 2], dss[8 * t + 3],
-                                        dss[8 * t + 4], dss[8 * t + 5], dss[8 * t + 6], dss[8 * t + 7]);
+          const bf16x8 pa = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
+                                        s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
+          const bf16x8 da = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                                        dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
           const int rbase = (qb * 32 + 16 * t + tr_row) * ROW + tr_col;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const uint16_t* pg = g_s + rbase + db * 32;
-            const uint16_t* pq = q_s + rbase + db * 32;
+            const uint16_t* pg = sG + rbase + db * 32;
+            const uint16_t* pq = sQ + rbase + db * 32;
             const bf16x8 gb = join_u32x2(lds_read_tr16(pg), lds_read_tr16(pg + 8 * ROW));
             const bf16x8 qbv = join_u32x2(lds_read_tr16(pq), lds_read_tr16(pq + 8 * ROW));
             dv[db] = mfma_bf16(pa, gb, dv[db]);
             dk[db] = mfma_bf16(da, qbv, dk[db]);
           }
         }
-
-      // dS^T into LDS: row = key of this wave, 4 consecutive query rows per write.
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        // dS^T into LDS: row = key of this wave, 4 consecutive query rows per write.
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x16& dss = dp[qb];
-          u32x2 w = {pack_bf16x2(dss[4 * g + 0], dss[4 * g + 1]), pack_bf16x2(dss[4 * g + 2], dss[4 * g + 3])};
+          u32x2 w = {pack_bf16x2(dp[4 * g + 0], dp[4 * g + 1]), pack_bf16x2(dp[4 * g + 2], dp[4 * g + 3])};
           *(u32x2*)(sDS + (wave * 32 + l32) * SROW + qb * 32 + g * 8 + hi * 4) = w;
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     } else {
       u32x2 z = {0u, 0u};
 #pragma unroll
@@ -293,11 +277,15 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
     }
     __syncthreads();
 
+    // Every wave is past its last read of sQ / sG / sL / sDv: refill them now.
+    if (it + 1 < n_qt) store_tile();
+
     // dQ tile contribution: dQ[q][d] += sum over this workgroup's keys of dS[q][key] K[key][d].
     {
       int kmax = BK;
       if (CAUSAL) kmax = min(BK, q0 + BQ - k0);  // keys past the tile's last query have dS = 0
       const int nks = (kmax + 15) / 16;
+      const bool full_tile = q0 + BQ <= len;
 #pragma unroll
       for (int ui = 0; ui < DQ_UNITS / NW; ++ui) {
         const int unit = wave + ui * NW;
@@ -311,16 +299,20 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
           const bf16x8 bv = join_u32x2(lds_read_tr16(pb), lds_read_tr16(pb + 8 * ROW));
           acc = mfma_bf16(av, bv, acc);
         }
-        float* dqp = a.dq_acc + sv.base + db * 32 + l32;
+        float* dqp = a.dq_acc + sv.base + (int64_t)(q0 + qb * 32 + hi * 4) * sv.tok_stride + db * 32 + l32;
+        if (full_tile) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          if (qi < len) unsafeAtomicAdd(dqp + (int64_t)qi * sv.tok_stride, acc[r]);
+          for (int r = 0; r < 16; ++r)
+            unsafeAtomicAdd(dqp + (int64_t)((r >> 2) * 8 + (r & 3)) * sv.tok_stride, acc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            if (qi < len) unsafeAtomicAdd(dqp + (int64_t)((r >> 2) * 8 + (r & 3)) * sv.tok_stride, acc[r]);
+          }
         }
       }
     }
-
-    if (it + 1 < n_qt) store_tile(buf ^ 1);
     __syncthreads();
   }
 
