@@ -10,7 +10,12 @@ Workload (default): causal self-attention, B=4, H=32, N=4096, d=128, bf16,
 scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) rounded to bf16, seed 0.
 
 FLOP accounting: forward 4*B*H*N^2*d, halved under the causal mask; backward
-2.5x the forward (five N^2*d products, the recompute of S included).
+2.5x the forward (five N^2*d products, the recompute of S included).  The
+backward runs as three kernels: the D pre-pass (HBM-bound), the key-tile pass
+for dK/dV (four N^2*d products: S, dP, dV, dK; 2.0x the forward) and the
+query-tile pass for dQ (three: S, dP, dQ; 1.5x the forward).  Per-kernel
+rates below use the products each kernel executes; the backward TFLOP/s
+uses the method's 2.5x.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -135,7 +140,7 @@ def main(argv=None):
         M.attn_bwd_dkdv(q, k, v, lse, do, dk, dv, scale, causal, ws, stream)
         if ev is not None:
             ev[3].record(stream)
-        M.attn_bwd_dq(dq, scale, ws, stream)
+        M.attn_bwd_dq(q, k, v, lse, do, dq, scale, causal, ws, stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -153,11 +158,11 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per = {"fwd": [], "bwd_prep": [], "bwd_main": [], "bwd_dq": [], "step": []}
+    per = {"fwd": [], "bwd_prep": [], "bwd_dkdv": [], "bwd_dq": [], "step": []}
     for ev in events:
         per["fwd"].append(ev[0].elapsed_time(ev[1]))
         per["bwd_prep"].append(ev[1].elapsed_time(ev[2]))
-        per["bwd_main"].append(ev[2].elapsed_time(ev[3]))
+        per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
         per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
         per["step"].append(ev[0].elapsed_time(ev[4]))
     mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
@@ -165,17 +170,25 @@ def main(argv=None):
 
     f_fwd, f_bwd = flops(B, H, N, d, causal)
     ms_step = wall * 1e3 / args.steps
-    bwd_ms = mean["bwd_prep"] + mean["bwd_main"] + mean["bwd_dq"]
+    bwd_ms = mean["bwd_prep"] + mean["bwd_dkdv"] + mean["bwd_dq"]
+    f_dkdv, f_dq = 2.0 * f_fwd, 1.5 * f_fwd
     tflops_fwd = f_fwd / (mean["fwd"] * 1e-3) / 1e12
     tflops_bwd = f_bwd / (bwd_ms * 1e-3) / 1e12
-    tflops_main = f_bwd / (mean["bwd_main"] * 1e-3) / 1e12
+    tflops_dkdv = f_dkdv / (mean["bwd_dkdv"] * 1e-3) / 1e12
+    tflops_dq = f_dq / (mean["bwd_dq"] * 1e-3) / 1e12
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
     elem = B * H * N * d
     rows = B * H * N
-    prep_bytes = 2 * elem * 2 + rows * 4 + elem * 4       # read O, dO; write D; zero the dQ accumulator
-    dq_bytes = elem * 4 + elem * 2                         # read fp32 accumulator, write bf16 dQ
+    prep_bytes = 2 * elem * 2 + rows * 4                  # read O, dO; write D
     fwd_bytes = 3 * elem * 2 + elem * 2 + rows * 4         # read Q, K, V; write O, LSE
+    # dominant kernel for the roofline: the longest of the three MFMA kernels
+    kern = {"fwd_bf16_kernel (attn_fwd)": (mean["fwd"], f_fwd),
+            "bwd_dkdv_kernel (attn_bwd_dkdv)": (mean["bwd_dkdv"], f_dkdv),
+            "bwd_dq_kernel (attn_bwd_dq)": (mean["bwd_dq"], f_dq)}
+    dom = max(kern, key=lambda k_: kern[k_][0])
+    dom_ms, dom_flops = kern[dom]
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
 
     result = {
         "metric": METRIC if args.workload == DEFAULT else f"attn fwd+bwd TFLOPS, {args.workload}, 1 MI355X",
@@ -198,17 +211,15 @@ def main(argv=None):
                 "gbps": round(fwd_bytes / (mean["fwd"] * 1e-3) / 1e9, 1)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
                 "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2),
-                "main_ms": round(mean["bwd_main"], 4),
                 "prep_ms": round(mean["bwd_prep"], 4),
                 "prep_gbps": round(prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9, 1),
                 "prep_pct_hbm_peak": round(100 * prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-                "dq_ms": round(mean["bwd_dq"], 4),
-                "dq_gbps": round(dq_bytes / (mean["bwd_dq"] * 1e-3) / 1e9, 1),
-                "dq_pct_hbm_peak": round(100 * dq_bytes / (mean["bwd_dq"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)},
-        "roofline": {"kernel": "bwd_main_kernel (attn_bwd_dkdv)", "bound": "mfma",
-                     "achieved": round(tflops_main, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops_main / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "flops_per_launch": f_bwd, "avg_launch_ms": round(mean["bwd_main"], 4)},
+                "dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
+                "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2)},
+        "roofline": {"kernel": dom, "bound": "mfma",
+                     "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

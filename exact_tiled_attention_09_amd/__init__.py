@@ -6,7 +6,7 @@ script.  Functions carry the C names and take device tensors:
 
     attn_fwd, attn_bwd, attn_bwd_workspace_bytes,
     attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq,
-    attn_fwd_f32, attn_bwd_f32,
+    attn_fwd_f32, attn_bwd_f32, attn_bwd_f32_workspace_bytes,
     attn_fwd_varlen, attn_bwd_varlen, attn_bwd_varlen_workspace_bytes
 """
 from ._lib import (  # noqa: F401
@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_f32,
+    attn_bwd_f32_workspace_bytes,
     attn_bwd_preprocess,
     attn_bwd_varlen,
     attn_bwd_varlen_workspace_bytes,

@@ -30,10 +30,11 @@ SIGNATURES = {
     "miattn_status_string": (ctypes.c_char_p, [_I]),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_bwd_f32_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_bwd_preprocess": (_I, [_P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "attn_bwd_dkdv": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
-    "attn_bwd_dq": (_I, [_P, _I, _I, _I, _I, _F, _P, _S, _P]),
+    "attn_bwd_dq": (_I, [_P] * 6 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_f32": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_varlen": (_I, [_P] * 5 + [_P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
@@ -138,10 +139,15 @@ def attn_bwd_dkdv(q, k, v, lse, dO, dk, dv, scale: float, causal: bool, workspac
                                                  _stream(stream)))
 
 
-def attn_bwd_dq(dq, scale: float, workspace, stream=None):
-    B, H, N, d = _dense_dims(dq)
-    _check("attn_bwd_dq", load().attn_bwd_dq(_ptr(dq), B, H, N, d, float(scale), _ptr(workspace),
+def attn_bwd_dq(q, k, v, lse, dO, dq, scale: float, causal: bool, workspace, stream=None):
+    B, H, N, d = _dense_dims(q)
+    _check("attn_bwd_dq", load().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(dq), B, H, N, d,
+                                             float(scale), int(bool(causal)), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().attn_bwd_f32_workspace_bytes(B, H, N, d))
 
 
 def attn_fwd_f32(q, k, v, o, lse, scale: float, causal: bool, stream=None):

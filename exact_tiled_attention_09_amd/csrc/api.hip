@@ -19,8 +19,11 @@ bool ptr16(const void* p) { return p != nullptr && aligned(p, 16); }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: fp32 D (rows entries) then the fp32 dQ accumulator (rows * d).
-size_t workspace_bytes_for(int64_t rows, int d) {
+// bf16 backward workspace: fp32 D, one entry per row.
+size_t workspace_bytes_for(int64_t rows) { return round_up((size_t)rows * sizeof(float), 256); }
+
+// fp32 backward workspace: fp32 D, then an fp32 dQ accumulator (rows * d).
+size_t workspace_bytes_f32(int64_t rows, int d) {
   return round_up((size_t)rows * sizeof(float), 256) + (size_t)rows * (size_t)d * sizeof(float);
 }
 
@@ -93,7 +96,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_dense(B, H, N, d, 1.0f) != MIATTN_OK) return 0;
-  return workspace_bytes_for((int64_t)B * H * N, d);
+  return workspace_bytes_for((int64_t)B * H * N);
+}
+
+size_t attn_bwd_f32_workspace_bytes(int B, int H, int N, int d) {
+  if (check_dense(B, H, N, d, 1.0f) != MIATTN_OK) return 0;
+  return workspace_bytes_f32((int64_t)B * H * N, d);
 }
 
 int attn_bwd_preprocess(const void* o, const void* dO, int B, int H, int N, int d, void* workspace,
@@ -101,7 +109,7 @@ int attn_bwd_preprocess(const void* o, const void* dO, int B, int H, int N, int 
   if (!ptr16(o) || !ptr16(dO) || !ptr16(workspace)) return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, 1.0f)) return st;
   const int64_t rows = (int64_t)B * H * N;
-  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
   AttnArgs a = dense_args(nullptr, nullptr, nullptr, o, nullptr, B, H, N, 1.0f);
   a.dout = dO;
   carve(a, workspace, rows);
@@ -116,25 +124,28 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
     return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, scale)) return st;
   const int64_t rows = (int64_t)B * H * N;
-  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
   AttnArgs a = dense_args(q, k, v, nullptr, lse, B, H, N, scale);
   a.dout = dO;
   a.dk = dk;
   a.dv = dv;
   carve(a, workspace, rows);
-  return hip_status(miattn::launch_bwd_main_bf16(a, d, causal != 0, false, stream));
+  return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream));
 }
 
-int attn_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace, size_t workspace_bytes,
+int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dq, int B,
+                int H, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-  if (!ptr16(dq) || !ptr16(workspace)) return MIATTN_ERR_INVALID_ARG;
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, scale)) return st;
   const int64_t rows = (int64_t)B * H * N;
-  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
-  AttnArgs a = dense_args(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, N, scale);
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, nullptr, lse, B, H, N, scale);
+  a.dout = dO;
   a.dq = dq;
   carve(a, workspace, rows);
-  return hip_status(miattn::launch_bwd_dq_bf16(a, d, false, stream));
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
@@ -145,7 +156,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, scale)) return st;
   const int64_t rows = (int64_t)B * H * N;
-  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
   AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
   a.dout = dO;
   a.dq = dq;
@@ -153,8 +164,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.dv = dv;
   carve(a, workspace, rows);
   if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_main_bf16(a, d, causal != 0, false, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_bf16(a, d, false, stream));
+  if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
@@ -173,7 +184,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
     return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, scale)) return st;
   const int64_t rows = (int64_t)B * H * N;
-  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < workspace_bytes_f32(rows, d)) return MIATTN_ERR_INVALID_ARG;
   AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
   a.dout = dO;
   a.dq = dq;
@@ -197,7 +208,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 
 size_t attn_bwd_varlen_workspace_bytes(int total_tokens, int H, int d) {
   if (total_tokens <= 0 || H <= 0 || (d != 64 && d != 128)) return 0;
-  return workspace_bytes_for((int64_t)total_tokens * H, d);
+  return workspace_bytes_for((int64_t)total_tokens * H);
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
@@ -209,7 +220,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
     return MIATTN_ERR_INVALID_ARG;
   if (int st = check_varlen(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, scale)) return st;
   const int64_t rows = (int64_t)total_tokens * H;
-  if (workspace_bytes < workspace_bytes_for(rows, d)) return MIATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
   AttnArgs a = dense_args(q, k, v, o, lse, nseq, H, max_seqlen, scale);
   a.dout = dO;
   a.dq = dq;
@@ -220,8 +231,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.total_tokens = total_tokens;
   carve(a, workspace, rows);
   if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, true, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_main_bf16(a, d, causal != 0, true, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_bf16(a, d, true, stream));
+  if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, true, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, true, stream));
 }
 
 }  // extern "C"

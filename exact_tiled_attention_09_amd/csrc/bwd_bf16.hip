@@ -3,20 +3,30 @@
 // Method ("解析 FlashAttention（4）：FlashAttention-v2", section 五: the softmax
 // gradient 5.1, the D identity 5.2 and the general backward 5.4; the LSE
 // reconstruction of "分块 Attention：重建概率，累计梯度", section 04):
-//   D = rowsum(dO o O);  P = exp(S - LSE);  dV += P^T dO;  dP = dO V^T;
-//   dS = P o (dP - D);  dQ += scale dS K;  dK += scale dS^T Q.
+//   D = rowsum(dO o O);  P = exp(S - LSE);  dV = P^T dO;  dP = dO V^T;
+//   dS = P o (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
 //
 // Three kernels, all on the caller's stream:
-//  1. bwd_prep: D for every row (fp32) and a zeroed fp32 dQ accumulator.
-//  2. bwd_main: one workgroup per (sequence, head, 128-key tile); each of the
-//     4 waves owns 32 keys with their dK/dV accumulators in registers; the
-//     workgroup's K and V stay in LDS as MFMA operands.  For every 64-row query tile at or after the
-//     diagonal it recomputes S = Q K^T, P, dP = dO V^T and dS, accumulates
-//     dV += P^T dO and dK += dS^T Q (P/dS come straight out of the accumulator
-//     in A-operand layout; dO and Q are fed through the LDS transpose read),
-//     parks dS^T in LDS and forms the tile's dQ contribution, which it adds
-//     to the fp32 accumulator with hardware float atomics.
-//  3. bwd_dq: dQ = bf16(scale * accumulator).
+//  1. bwd_prep: D for every row, in fp32.
+//  2. bwd_dkdv: key-tile outer loop (the pages' loop order for dK and dV):
+//     one workgroup per (sequence, head, 128-key tile); each of 4 waves owns
+//     32 keys and keeps their dK/dV accumulators in registers.  For every
+//     64-row query tile at or after the diagonal it rebuilds S = Q K^T and
+//     P = exp(S - LSE), forms dP = dO V^T and dS, and accumulates dV += P^T dO
+//     and dK += dS^T Q.  S and dS leave the accumulator already in A-operand
+//     layout (lane = key); dO and Q enter through the LDS transpose read.
+//  3. bwd_dq: query-tile outer loop, shaped like the forward: one workgroup
+//     per (sequence, head, 256-row query tile), 8 waves of 32 rows with Q and
+//     dO resident in registers.  For every key tile up to the diagonal it
+//     rebuilds S^T = K Q^T and dP^T = V dO^T (lane = query, so LSE and D are
+//     per-lane scalars) and accumulates dQ^T += K^T dS^T.
+// The pages accumulate dQ with atomic adds from the key-tile loop.  Here dQ
+// gets its own pass instead: it re-forms S and dP (two more N^2 d products),
+// but on MI355X device-scope float atomics are performed past the per-XCD L2,
+// and at B4 H32 N4096 d128 they moved 4.7 GB per backward through memory.
+// The split also makes dQ, like dK and dV, bitwise reproducible.
+//
+// All K / V / Q / dO tiles in LDS use the XOR swizzle of swz<D>.
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
@@ -24,8 +34,8 @@ namespace miattn {
 
 // ---------------------------------------------------------------- kernel 1
 // Rows are (batch, head, token) for dense tensors and (token, head) for packed
-// ones; both flatten to row r with features at r*D in memory order, except
-// that D is stored like LSE ([B,H,N] or [H,T]).
+// ones; both flatten to row r with features at r*D in memory order, while D is
+// stored like LSE ([B,H,N] or [H,T]).
 template <int D, bool VARLEN>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows) {
   constexpr int LPR = D / 8;        // lanes per row, 16 bytes each
@@ -44,9 +54,6 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows)
       acc = __builtin_fmaf(bf16_bits_to_f32(o[w] & 0xffffu), bf16_bits_to_f32(g[w] & 0xffffu), acc);
       acc = __builtin_fmaf(bf16_bits_to_f32(o[w] >> 16), bf16_bits_to_f32(g[w] >> 16), acc);
     }
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(a.dq_acc + off) = z;
-    *(f32x4*)(a.dq_acc + off + 4) = z;
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
@@ -61,33 +68,23 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows)
 }
 
 // ---------------------------------------------------------------- kernel 2
-// LDS holds the workgroup's K and V tiles for its whole life (row-major, read
-// as MFMA operands), one Q / dO tile (refilled while the dQ product runs: the
-// barrier before that product is the last point any wave reads them), and the
-// dS^T tile.  Per wave, registers hold only the dK/dV accumulators and the
-// S/dP tiles, so everything fits the 256 architectural VGPRs.
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktiles) {
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NW = 4;
   constexpr int BK = NW * 32;        // keys per workgroup
   constexpr int BQ = 64;             // query rows per step
   constexpr int KS = D / 16;         // k-steps over the head dim
   constexpr int DB = D / 32;
-  constexpr int ROW = D + 16;        // padded bf16 row of Q / dO / K / V tiles
-  constexpr int SROW = BQ + 16;      // padded bf16 row of the dS^T tile
   constexpr int CH_PER_ROW = D / 8;
   constexpr int QCPT = BQ * CH_PER_ROW / 256;  // 16-byte chunks per thread, Q tile
   constexpr int KCPT = BK * CH_PER_ROW / 256;
-  constexpr int DQ_UNITS = 2 * DB;   // (32-row block, 32-col block) pairs of a dQ tile
-  static_assert(DQ_UNITS % NW == 0, "dQ units must split evenly over the waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BK * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BK * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[BQ * ROW];    // dO
-  __shared__ __attribute__((aligned(16))) uint16_t sDS[BK * SROW];  // dS^T, bf16
-  __shared__ __attribute__((aligned(16))) float sL[BQ];             // LSE * log2(e), +inf if dead
-  __shared__ __attribute__((aligned(16))) float sDv[BQ];            // D
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BQ * D];   // dO
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];          // LSE * log2(e), +inf if dead
+  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];         // D
 
   const int nbh = a.B * a.H;
   const int bh = blockIdx.x % nbh;
@@ -97,7 +94,6 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
   const SeqView sv = seq_view<VARLEN>(a, b, h, D);
   const int k0 = kt * BK;
   if (k0 >= sv.len) return;
-  (void)n_ktiles;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -120,7 +116,7 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
   }
   const bool any_bad_key = wave_any(!key_ok);
 
-  // The workgroup's K and V tiles, row-major (rows past the sequence are zero).
+  // The workgroup's K and V tiles (rows past the sequence are zero).
 #pragma unroll
   for (int cidx = 0; cidx < KCPT; ++cidx) {
     const int chunk = tid + cidx * 256;
@@ -132,8 +128,9 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
       xk = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
       xv = *(const u32x4*)(vp + (int64_t)key * sv.tok_stride + col);
     }
-    *(u32x4*)(sK + row * ROW + col) = xk;
-    *(u32x4*)(sV + row * ROW + col) = xv;
+    const int off = swz_off<D>(row, col);
+    *(u32x4*)(sK + off) = xk;
+    *(u32x4*)(sV + off) = xv;
   }
 
   f32x16 dk[DB], dv[DB];
@@ -146,6 +143,13 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
   const int n_qt = (len + BQ - 1) / BQ;
   const int qt_begin = CAUSAL ? k0 / BQ : 0;
 
+  int st_off[QCPT];
+#pragma unroll
+  for (int cidx = 0; cidx < QCPT; ++cidx) {
+    const int chunk = tid + cidx * 256;
+    const int row = chunk / CH_PER_ROW;
+    st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
+  }
   u32x4 rq[QCPT], rg[QCPT];
   float rl = 0.f, rd = 0.f;
   auto load_tile = [&](int it) {
@@ -175,35 +179,40 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int cidx = 0; cidx < QCPT; ++cidx) {
-      const int chunk = tid + cidx * 256;
-      const int row = chunk / CH_PER_ROW;
-      const int col = (chunk - row * CH_PER_ROW) * 8;
-      *(u32x4*)(&sQ[row * ROW + col]) = rq[cidx];
-      *(u32x4*)(&sG[row * ROW + col]) = rg[cidx];
+      *(u32x4*)(&sQ[buf][st_off[cidx]]) = rq[cidx];
+      *(u32x4*)(&sG[buf][st_off[cidx]]) = rg[cidx];
     }
     if (tid < BQ) {
-      sL[tid] = rl;
-      sDv[tid] = rd;
+      sL[buf][tid] = rl;
+      sDv[buf][tid] = rd;
     }
   };
 
+  // Per-lane operand offsets (a row's swizzle depends only on the row mod 16).
+  int aoff[KS];       // b128 operand rows (query or key) l32, chunk 2*ks + hi
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aoff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
+  const int tr_r = hi * 4 + ((lane >> 2) & 3);
+  const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  int troff[2][DB];   // transpose reads: rows 8R + tr_r, columns db*32 + tr_c
+#pragma unroll
+  for (int R = 0; R < 2; ++R)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
+  const uint16_t* kb_rows = sK + wave * 32 * D;
+  const uint16_t* vb_rows = sV + wave * 32 * D;
+
   if (qt_begin < n_qt) {
     load_tile(qt_begin);
-    store_tile();
+    store_tile(0);
   }
   __syncthreads();
 
-  // Transpose-read addressing shared by every "rows of 4 x 16" operand.
-  const int tr_row = hi * 4 + ((lane >> 2) & 3);
-  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  // B operands of S = Q K^T and dP = dO V^T: lane = this wave's key, 8 features.
-  const uint16_t* kb_row = sK + (wave * 32 + l32) * ROW + hi * 8;
-  const uint16_t* vb_row = sV + (wave * 32 + l32) * ROW + hi * 8;
-
   for (int it = qt_begin; it < n_qt; ++it) {
+    const int buf = (it - qt_begin) & 1;
     const int q0 = it * BQ;
     if (it + 1 < n_qt) load_tile(it + 1);
 
@@ -211,23 +220,26 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
     if (live) {
       bool need_mask = (wk0 + 31 >= len) || any_bad_key;
       if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0);
+      const uint16_t* q_s = sQ[buf];
+      const uint16_t* g_s = sG[buf];
       // One 32-row half of the query tile at a time keeps S and dP to 32
       // registers; the scheduling barriers stop the halves from interleaving.
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         __builtin_amdgcn_sched_barrier(0);
+        if (CAUSAL && q0 + qb * 32 + 31 < wk0) continue;  // this half sees none of the wave's keys
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int off = (qb * 32 + l32) * ROW + ks * 16 + hi * 8;
-          s = mfma_bf16(as_bf16x8(*(const u32x4*)(sQ + off)), as_bf16x8(*(const u32x4*)(kb_row + ks * 16)), s);
-          dp = mfma_bf16(as_bf16x8(*(const u32x4*)(sG + off)), as_bf16x8(*(const u32x4*)(vb_row + ks * 16)), dp);
+          const int off = qb * 32 * D + aoff[ks];
+          s = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks])), s);
+          dp = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks])), dp);
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + g * 8 + hi * 4;
-          const f32x4 lv = *(const f32x4*)(&sL[ql]);
-          const f32x4 dvv = *(const f32x4*)(&sDv[ql]);
+          const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
+          const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = g * 4 + e;
@@ -248,71 +260,22 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
                                         s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
           const bf16x8 da = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
                                         dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-          const int rbase = (qb * 32 + 16 * t + tr_row) * ROW + tr_col;
+          const int rbase = (qb * 32 + 16 * t) * D;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const uint16_t* pg = sG + rbase + db * 32;
-            const uint16_t* pq = sQ + rbase + db * 32;
-            const bf16x8 gb = join_u32x2(lds_read_tr16(pg), lds_read_tr16(pg + 8 * ROW));
-            const bf16x8 qbv = join_u32x2(lds_read_tr16(pq), lds_read_tr16(pq + 8 * ROW));
+            const bf16x8 gb = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]),
+                                         lds_read_tr16(g_s + rbase + troff[1][db]));
+            const bf16x8 qbv = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]),
+                                          lds_read_tr16(q_s + rbase + troff[1][db]));
             dv[db] = mfma_bf16(pa, gb, dv[db]);
             dk[db] = mfma_bf16(da, qbv, dk[db]);
           }
         }
-        // dS^T into LDS: row = key of this wave, 4 consecutive query rows per write.
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w = {pack_bf16x2(dp[4 * g + 0], dp[4 * g + 1]), pack_bf16x2(dp[4 * g + 2], dp[4 * g + 3])};
-          *(u32x2*)(sDS + (wave * 32 + l32) * SROW + qb * 32 + g * 8 + hi * 4) = w;
-        }
       }
       __builtin_amdgcn_sched_barrier(0);
-    } else {
-      u32x2 z = {0u, 0u};
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(u32x2*)(sDS + (wave * 32 + l32) * SROW + qb * 32 + g * 8 + hi * 4) = z;
     }
-    __syncthreads();
 
-    // Every wave is past its last read of sQ / sG / sL / sDv: refill them now.
-    if (it + 1 < n_qt) store_tile();
-
-    // dQ tile contribution: dQ[q][d] += sum over this workgroup's keys of dS[q][key] K[key][d].
-    {
-      int kmax = BK;
-      if (CAUSAL) kmax = min(BK, q0 + BQ - k0);  // keys past the tile's last query have dS = 0
-      const int nks = (kmax + 15) / 16;
-      const bool full_tile = q0 + BQ <= len;
-#pragma unroll
-      for (int ui = 0; ui < DQ_UNITS / NW; ++ui) {
-        const int unit = wave + ui * NW;
-        const int qb = unit / DB;
-        const int db = unit - qb * DB;
-        f32x16 acc = f32x16{};
-        for (int ks = 0; ks < nks; ++ks) {
-          const uint16_t* pa = sDS + (ks * 16 + tr_row) * SROW + qb * 32 + tr_col;
-          const uint16_t* pb = sK + (ks * 16 + tr_row) * ROW + db * 32 + tr_col;
-          const bf16x8 av = join_u32x2(lds_read_tr16(pa), lds_read_tr16(pa + 8 * SROW));
-          const bf16x8 bv = join_u32x2(lds_read_tr16(pb), lds_read_tr16(pb + 8 * ROW));
-          acc = mfma_bf16(av, bv, acc);
-        }
-        float* dqp = a.dq_acc + sv.base + (int64_t)(q0 + qb * 32 + hi * 4) * sv.tok_stride + db * 32 + l32;
-        if (full_tile) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            unsafeAtomicAdd(dqp + (int64_t)((r >> 2) * 8 + (r & 3)) * sv.tok_stride, acc[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            if (qi < len) unsafeAtomicAdd(dqp + (int64_t)((r >> 2) * 8 + (r & 3)) * sv.tok_stride, acc[r]);
-          }
-        }
-      }
-    }
+    if (it + 1 < n_qt) store_tile(buf ^ 1);
     __syncthreads();
   }
 
@@ -336,15 +299,208 @@ __global__ void __launch_bounds__(256, 1) bwd_main_kernel(AttnArgs a, int n_ktil
 }
 
 // ---------------------------------------------------------------- kernel 3
-__global__ void __launch_bounds__(256) bwd_dq_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
-                                                     int64_t n8, float scale) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 x0 = *(const f32x4*)(acc + i * 8);
-  const f32x4 x1 = *(const f32x4*)(acc + i * 8 + 4);
-  u32x4 w = {pack_bf16x2(x0[0] * scale, x0[1] * scale), pack_bf16x2(x0[2] * scale, x0[3] * scale),
-             pack_bf16x2(x1[0] * scale, x1[1] * scale), pack_bf16x2(x1[2] * scale, x1[3] * scale)};
-  *(u32x4*)(dq + i * 8) = w;
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
+__global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qtiles) {
+  constexpr int BC = 64;                 // keys per tile
+  constexpr int BR = NW * 32;            // query rows per workgroup
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = BC * D;
+  constexpr int NT = NW * 64;
+  constexpr int CH_PER_ROW = D / 8;
+  constexpr int CPT = BC * CH_PER_ROW / NT;
+  static_assert(CPT * NT == BC * CH_PER_ROW, "tile chunks must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+  __shared__ uint8_t s_valid[2][BC];
+  __shared__ uint32_t s_anypad[2];
+
+  const int nbh = a.B * a.H;
+  const int bh = blockIdx.x % nbh;
+  int tile = blockIdx.x / nbh;
+  if (CAUSAL) tile = n_qtiles - 1 - tile;  // heaviest query tiles first
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const SeqView sv = seq_view<VARLEN>(a, b, h, D);
+  const int q_tile0 = tile * BR;
+  if (q_tile0 >= sv.len) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int q_wave0 = q_tile0 + wave * 32;
+  const int qi = q_wave0 + l32;  // this lane's query row (columns of S^T)
+  const float c = a.scale_log2;
+
+  const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ gp = (const uint16_t*)a.dout + sv.base;
+
+  // Q and dO as B operands (lane = query, 8 features per k-step).
+  bf16x8 qf[KS], gf[KS];
+  const bool row_ok = qi < sv.len;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+      x = *(const u32x4*)(qp + (int64_t)qi * sv.tok_stride + ks * 16 + hi * 8);
+      y = *(const u32x4*)(gp + (int64_t)qi * sv.tok_stride + ks * 16 + hi * 8);
+    }
+    qf[ks] = as_bf16x8(x);
+    gf[ks] = as_bf16x8(y);
+  }
+  float lse2 = kPosInf, dd = 0.f;  // a dead or out-of-range row gets P = 0
+  if (row_ok) {
+    const float lse = a.lse[sv.row_base + qi];
+    lse2 = (lse == kNegInf) ? kPosInf : lse * kLog2e;
+    dd = a.dvec[sv.row_base + qi];
+  }
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+
+  const int kv_len = sv.len;
+  const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  int st_off[CPT];
+#pragma unroll
+  for (int cidx = 0; cidx < CPT; ++cidx) {
+    const int chunk = tid + cidx * NT;
+    const int row = chunk / CH_PER_ROW;
+    st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
+  }
+  u32x4 rk[CPT], rv[CPT];
+  uint32_t rvalid = 1u;
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int cidx = 0; cidx < CPT; ++cidx) {
+      const int chunk = tid + cidx * NT;
+      const int row = chunk / CH_PER_ROW;
+      const int col = (chunk - row * CH_PER_ROW) * 8;
+      const int key = j * BC + row;
+      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+      if (key < kv_len) {
+        zk = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
+        zv = *(const u32x4*)(vp + (int64_t)key * sv.tok_stride + col);
+      }
+      rk[cidx] = zk;
+      rv[cidx] = zv;
+    }
+    if constexpr (KPAD) {
+      if (wave == 0) {
+        const int key = j * BC + lane;
+        rvalid = (key < kv_len) ? (uint32_t)(a.key_valid[sv.tok0 + key] != 0) : 1u;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* sk = smem + buf * 2 * TILE;
+    uint16_t* sv_ = sk + TILE;
+#pragma unroll
+    for (int cidx = 0; cidx < CPT; ++cidx) {
+      *(u32x4*)(sk + st_off[cidx]) = rk[cidx];
+      *(u32x4*)(sv_ + st_off[cidx]) = rv[cidx];
+    }
+    if constexpr (KPAD) {
+      if (wave == 0) {
+        s_valid[buf][lane] = (uint8_t)rvalid;
+        const bool any = wave_any(rvalid == 0u);
+        if (lane == 0) s_anypad[buf] = any ? 1u : 0u;
+      }
+    }
+  };
+
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
+  const int tr_r = hi * 4 + ((lane >> 2) & 3);
+  const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  int troff[2][DB];
+#pragma unroll
+  for (int R = 0; R < 2; ++R)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+
+    const int kt0 = j * BC;
+    const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
+    if (wave_live) {
+      const uint16_t* sk = smem + buf * 2 * TILE;
+      const uint16_t* svv = sk + TILE;
+      bool need_mask = kt0 + BC > kv_len;
+      if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
+      if (KPAD) need_mask = need_mask || (s_anypad[buf] != 0u);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (CAUSAL && kt0 + kb * 32 > q_wave0 + 31) continue;  // block wholly above the diagonal
+        // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query column).
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s);
+          dp = mfma_bf16(as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks])), gf[ks], dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+          if (need_mask) {
+            const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            const int key = kt0 + kl;
+            bool vis = key < kv_len;
+            if (CAUSAL) vis = vis && key <= qi;
+            if (KPAD) vis = vis && s_valid[buf][kl] != 0;
+            p = vis ? p : 0.f;
+          }
+          dp[r] = p * (dp[r] - dd);
+        }
+        // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read.
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 dsb = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                                         dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
+          const uint16_t* kt = sk + (kb * 32 + 16 * t) * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 ka = join_u32x2(lds_read_tr16(kt + troff[0][db]), lds_read_tr16(kt + troff[1][db]));
+            dq[db] = mfma_bf16(ka, dsb, dq[db]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers = features).
+  if (row_ok) {
+    uint16_t* __restrict__ dqp = (uint16_t*)a.dq + sv.base + (int64_t)qi * sv.tok_stride;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& x = dq[db];
+        u32x2 w = {pack_bf16x2(x[4 * g + 0] * a.scale, x[4 * g + 1] * a.scale),
+                   pack_bf16x2(x[4 * g + 2] * a.scale, x[4 * g + 3] * a.scale)};
+        *(u32x2*)(dqp + db * 32 + g * 8 + hi * 4) = w;
+      }
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -367,42 +523,51 @@ hipError_t launch_bwd_prep_bf16(const AttnArgs& a, int d, bool varlen, hipStream
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
-static hipError_t launch_bwd_main_t(const AttnArgs& a, hipStream_t stream) {
+static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BK = 128;
-  const int n_ktiles = (a.N + BK - 1) / BK;
-  const int64_t blocks = (int64_t)n_ktiles * a.B * a.H;
+  const int64_t blocks = (int64_t)((a.N + BK - 1) / BK) * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     a, n_ktiles);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t dispatch_bwd_main(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
-  if (varlen) {
-    if (causal) return kpad ? launch_bwd_main_t<D, true, true, true>(a, s) : launch_bwd_main_t<D, true, true, false>(a, s);
-    return kpad ? launch_bwd_main_t<D, false, true, true>(a, s) : launch_bwd_main_t<D, false, true, false>(a, s);
-  }
-  return causal ? launch_bwd_main_t<D, true, false, false>(a, s) : launch_bwd_main_t<D, false, false, false>(a, s);
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
+static hipError_t launch_dq_t(const AttnArgs& a, hipStream_t stream) {
+  constexpr int NW = 8;
+  constexpr int BR = NW * 32;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                     a, n_qtiles);
+  return hipGetLastError();
 }
 
-hipError_t launch_bwd_main_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream) {
+template <int D, bool DQ>
+static hipError_t dispatch_bwd(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
+#define MIATTN_BWD_LAUNCH(C, V, K) (DQ ? launch_dq_t<D, C, V, K>(a, s) : launch_dkdv_t<D, C, V, K>(a, s))
+  if (varlen) {
+    if (causal) return kpad ? MIATTN_BWD_LAUNCH(true, true, true) : MIATTN_BWD_LAUNCH(true, true, false);
+    return kpad ? MIATTN_BWD_LAUNCH(false, true, true) : MIATTN_BWD_LAUNCH(false, true, false);
+  }
+  return causal ? MIATTN_BWD_LAUNCH(true, false, false) : MIATTN_BWD_LAUNCH(false, false, false);
+#undef MIATTN_BWD_LAUNCH
+}
+
+hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream) {
   const bool kpad = varlen && a.key_valid != nullptr;
-  if (d == 128) return dispatch_bwd_main<128>(a, causal, varlen, kpad, stream);
-  if (d == 64) return dispatch_bwd_main<64>(a, causal, varlen, kpad, stream);
+  if (d == 128) return dispatch_bwd<128, false>(a, causal, varlen, kpad, stream);
+  if (d == 64) return dispatch_bwd<64, false>(a, causal, varlen, kpad, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool varlen, hipStream_t stream) {
-  const int64_t elems = (varlen ? (int64_t)a.total_tokens : (int64_t)a.B * a.N) * a.H * d;
-  const int64_t n8 = elems / 8;
-  if (n8 <= 0) return hipSuccess;
-  const int64_t blocks = (n8 + 255) / 256;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const float*)a.dq_acc,
-                     (uint16_t*)a.dq, n8, a.scale);
-  return hipGetLastError();
+hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream) {
+  const bool kpad = varlen && a.key_valid != nullptr;
+  if (d == 128) return dispatch_bwd<128, true>(a, causal, varlen, kpad, stream);
+  if (d == 64) return dispatch_bwd<64, true>(a, causal, varlen, kpad, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace miattn

@@ -17,7 +17,9 @@
 //    O^T += V^T P^T; V^T comes from the row-major V tile through the LDS
 //    transpose read, so neither P nor V is shuffled.
 //  * K/V tiles of BC = 64 keys are double-buffered in LDS (one barrier per
-//    tile); Q stays in registers for the whole key loop.
+//    tile) in the XOR-swizzled layout of swz<D>, which keeps both the b128
+//    operand reads and the transpose reads free of bank conflicts; Q stays in
+//    registers for the whole key loop.
 //  * softmax runs in base 2 with scale * log2(e) folded into one FMA.  A row's
 //    reference max is only raised when a tile's max exceeds it by more than
 //    kLazyMax (base-2 units); below that the stale reference is kept, P~ stays
@@ -43,8 +45,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
   constexpr int BR = NW * QB * 32;       // query rows per workgroup
   constexpr int KS = D / 16;             // k-steps of S over the head dim
   constexpr int DB = D / 32;             // 32-wide blocks of O columns
-  constexpr int ROW = D + 16;            // padded LDS row, bf16 elements
-  constexpr int TILE = BC * ROW;         // one K or V tile
+  constexpr int TILE = BC * D;           // one K or V tile (swizzled rows, see swz)
   constexpr int NT = NW * 64;
   constexpr int CH_PER_ROW = D / 8;      // 16-byte chunks per row
   constexpr int CPT = BC * CH_PER_ROW / NT;
@@ -134,16 +135,20 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
       }
     }
   };
+  int st_off[CPT];  // swizzled LDS offset of each staged chunk
+#pragma unroll
+  for (int cidx = 0; cidx < CPT; ++cidx) {
+    const int chunk = tid + cidx * NT;
+    const int row = chunk / CH_PER_ROW;
+    st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
+  }
   auto store_tile = [&](int buf) {
     uint16_t* sk = smem + buf * 2 * TILE;
     uint16_t* sv_ = sk + TILE;
 #pragma unroll
     for (int cidx = 0; cidx < CPT; ++cidx) {
-      const int chunk = tid + cidx * NT;
-      const int row = chunk / CH_PER_ROW;
-      const int col = (chunk - row * CH_PER_ROW) * 8;
-      *(u32x4*)(sk + row * ROW + col) = rk[cidx];
-      *(u32x4*)(sv_ + row * ROW + col) = rv[cidx];
+      *(u32x4*)(sk + st_off[cidx]) = rk[cidx];
+      *(u32x4*)(sv_ + st_off[cidx]) = rv[cidx];
     }
     if constexpr (KPAD) {
       if (wave == 0) {
@@ -153,6 +158,19 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
       }
     }
   };
+
+  // Per-lane operand offsets inside a tile (the swizzle of a row depends only
+  // on the row modulo 16, so 32-row and 16-row steps reuse them).
+  int koff[KS];       // K as the A operand of S^T: row kb*32 + l32, chunk 2*ks + hi
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
+  const int tr_r = hi * 4 + ((lane >> 2) & 3);
+  const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  int voff[2][DB];    // V through the transpose read: rows 8R + tr_r, columns db*32 + tr_c
+#pragma unroll
+  for (int R = 0; R < 2; ++R)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) voff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
 
   if (ntiles > 0) {
     load_tile(0);
@@ -180,7 +198,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = as_bf16x8(*(const u32x4*)(sk + (kb * 32 + l32) * ROW + ks * 16 + hi * 8));
+          const bf16x8 ka = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16(ka, qf[qb][ks], s[kb][qb]);
         }
@@ -253,12 +271,10 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
             pb[qb] = pack_bf16x8(x[8 * t + 0], x[8 * t + 1], x[8 * t + 2], x[8 * t + 3],
                                  x[8 * t + 4], x[8 * t + 5], x[8 * t + 6], x[8 * t + 7]);
           }
-          const int key_row = kb * 32 + 16 * t + hi * 4 + ((lane >> 2) & 3);
-          const int col_in = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+          const uint16_t* vt = svt + (kb * 32 + 16 * t) * D;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const uint16_t* p0 = svt + key_row * ROW + db * 32 + col_in;
-            const bf16x8 va = join_u32x2(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * ROW));
+            const bf16x8 va = join_u32x2(lds_read_tr16(vt + voff[0][db]), lds_read_tr16(vt + voff[1][db]));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma_bf16(va, pb[qb], o[qb][db]);
           }

@@ -139,6 +139,29 @@ __device__ __forceinline__ float lane_xor32(float x) {
 __device__ __forceinline__ float wave_max_halves(float x) { return fmaxf(x, lane_xor32(x)); }
 __device__ __forceinline__ float wave_sum_halves(float x) { return x + lane_xor32(x); }
 
+// Swizzled LDS tiles.  A tile is row-major with rows of D bf16 elements and no
+// padding; the 16-byte chunk c of row r is stored at chunk c ^ swz<D>(r).
+// The XOR pattern makes both access shapes of the kernels conflict-free:
+//  * 16 consecutive rows reading the same logical chunk (b128 operand reads
+//    with lane = row) land on 16 distinct chunk slots of the 64 banks;
+//  * the transpose read (4 consecutive rows starting at a multiple of 4, four
+//    consecutive chunks starting at a multiple of 4) lands on 16 distinct
+//    chunk slots.
+// For D = 64 two rows share one 256-byte bank line, which the pattern for
+// D = 64 accounts for.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+  static_assert(D == 64 || D == 128, "swizzle defined for rows of 64 or 128 bf16");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of (row r, element col) in a swizzled tile with rows of D.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r)) << 3) | (col & 7));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -7,8 +7,8 @@ struct AttnArgs;
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const AttnArgs& a, int d, bool varlen, hipStream_t stream);
-hipError_t launch_bwd_main_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
-hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool varlen, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);

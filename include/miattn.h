@@ -83,36 +83,46 @@ const char* miattn_status_string(int status);
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
-/* Bytes of device workspace attn_bwd / attn_bwd_f32 need: fp32 D [B,H,N] and
- * an fp32 dQ accumulator [B,H,N,d].  Returns 0 for invalid sizes. */
+/* Bytes of device workspace attn_bwd and its stages need: fp32 D [B,H,N]
+ * (rounded up to 256 bytes).  Returns 0 for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Bytes of device workspace attn_bwd_f32 needs: fp32 D [B,H,N] and an fp32
+ * dQ accumulator [B,H,N,d].  Returns 0 for invalid sizes. */
+size_t attn_bwd_f32_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward, dense bf16.  Inputs q, k, v, o (from attn_fwd), lse (from
  * attn_fwd), dO: upstream gradient [B,H,N,d] bf16.  Outputs dq, dk, dv:
  * [B,H,N,d] bf16 (fp32 accumulation, one final rounding).  workspace: at least
  * attn_bwd_workspace_bytes(B,H,N,d) bytes, 16-byte aligned, no initial
  * contents required; it is overwritten.  The LSE receives no gradient.
- * Equivalent to attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq.
+ * Equivalent to attn_bwd_preprocess, then attn_bwd_dkdv and attn_bwd_dq (the
+ * last two are independent of each other).  The result is bitwise
+ * reproducible: no output is accumulated with atomics.
  * LSE-recompute backward of "解析 FlashAttention（4）" section 五. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dO, void* dq, void* dk, void* dv,
              int B, int H, int N, int d, float scale, int causal,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 1 of attn_bwd: D = rowsum(dO o O) in fp32 into the workspace and a
- * zeroed dQ accumulator ("解析 FlashAttention（4）" section 5.2). */
+/* Stage 1 of attn_bwd: D = rowsum(dO o O) in fp32 into the workspace
+ * ("解析 FlashAttention（4）" section 5.2). */
 int attn_bwd_preprocess(const void* o, const void* dO, int B, int H, int N, int d,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 2 of attn_bwd: one pass over key tiles that writes dk and dv and adds
- * every query tile's dQ contribution into the workspace accumulator
- * ("解析 FlashAttention（4）" section 5.4).  Needs stage 1 on the same workspace. */
+/* Stage 2 of attn_bwd: the key-tile outer loop that rebuilds P and dS and
+ * writes dk and dv ("解析 FlashAttention（4）" section 5.4).  Needs stage 1 on
+ * the same workspace. */
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
                   void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 3 of attn_bwd: dq = bf16(scale * accumulator). */
-int attn_bwd_dq(void* dq, int B, int H, int N, int d, float scale,
+/* Stage 3 of attn_bwd: a query-tile outer loop that rebuilds P and dS and
+ * writes dq = scale dS K ("解析 FlashAttention（4）" sections 5.3-5.4, with
+ * the dQ sum taken per query tile instead of by atomic adds).  Needs stage 1
+ * on the same workspace. */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dq,
+                int B, int H, int N, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* fp32 forward: same contract as attn_fwd with fp32 q, k, v, o. */
@@ -120,7 +130,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /* fp32 backward: same contract as attn_bwd with fp32 tensors; workspace size
- * from attn_bwd_workspace_bytes. */
+ * from attn_bwd_f32_workspace_bytes.  dq is accumulated with float atomics
+ * across key tiles, so it may differ in the last bits from run to run. */
 int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
                  const float* dO, float* dq, float* dk, float* dv,
                  int B, int H, int N, int d, float scale, int causal,
@@ -135,7 +146,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     int H, int d, float scale, int causal, const unsigned char* key_valid,
                     hipStream_t stream);
 
-/* Workspace bytes for attn_bwd_varlen: fp32 D [H,T] and dQ accumulator [T,H,d]. */
+/* Workspace bytes for attn_bwd_varlen: fp32 D [H,T]. */
 size_t attn_bwd_varlen_workspace_bytes(int total_tokens, int H, int d);
 
 /* Backward over packed variable-length sequences, bf16; arguments as in

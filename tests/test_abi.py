@@ -58,11 +58,11 @@ def test_workspace_sizes():
     lib = _lib()
     B, H, N, d = 4, 32, 4096, 128
     rows = B * H * N
-    want = (rows * 4 + 255) // 256 * 256 + rows * d * 4
-    assert lib.attn_bwd_workspace_bytes(B, H, N, d) == want
+    assert lib.attn_bwd_workspace_bytes(B, H, N, d) == (rows * 4 + 255) // 256 * 256
+    assert lib.attn_bwd_f32_workspace_bytes(B, H, N, d) == (rows * 4 + 255) // 256 * 256 + rows * d * 4
     assert lib.attn_bwd_workspace_bytes(B, H, N, 96) == 0
     assert lib.attn_bwd_workspace_bytes(0, H, N, d) == 0
-    assert lib.attn_bwd_varlen_workspace_bytes(1000, 32, 64) == (32000 * 4 + 255) // 256 * 256 + 32000 * 64 * 4
+    assert lib.attn_bwd_varlen_workspace_bytes(1000, 32, 64) == (32000 * 4 + 255) // 256 * 256
 
 
 # A fake, aligned, non-null "device" address: validation fails before it is used.
@@ -95,7 +95,8 @@ def test_backward_rejects_small_workspace():
     need = lib.attn_bwd_workspace_bytes(1, 2, 64, 64)
     st = lib.attn_bwd(*([FAKE] * 9), 1, 2, 64, 64, 0.125, 1, FAKE, need - 4, NULL)
     assert st == -1
-    st = lib.attn_bwd_f32(*([FAKE] * 9), 1, 2, 64, 64, 0.125, 1, FAKE, need - 4, NULL)
+    need32 = lib.attn_bwd_f32_workspace_bytes(1, 2, 64, 64)
+    st = lib.attn_bwd_f32(*([FAKE] * 9), 1, 2, 64, 64, 0.125, 1, FAKE, need32 - 4, NULL)
     assert st == -1
 
 

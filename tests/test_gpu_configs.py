@@ -184,7 +184,7 @@ def test_config1_fwd_bwd_f32(lib):
     lse = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
     lib.attn_fwd_f32(q, k, v, o, lse, 1 / 8, False)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(lib.attn_bwd_workspace_bytes(1, 1, 128, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.attn_bwd_f32_workspace_bytes(1, 1, 128, 64), dtype=torch.uint8, device="cuda")
     lib.attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, 1 / 8, False, ws)
     torch.cuda.synchronize()
     ref = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], 1 / 8, False)
