@@ -55,6 +55,32 @@ def flops(B, H, N, d, causal):
     return fwd, 2.5 * fwd
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_causal_b4_h32_n4096_d128.json")
+KERNEL_KEYS = {"fwd_bf16_kernel (attn_fwd)": "fwd_bf16_kernel",
+               "bwd_dkdv_kernel (attn_bwd_dkdv)": "bwd_dkdv_kernel",
+               "bwd_dq_kernel (attn_bwd_dq)": "bwd_dq_kernel"}
+
+
+def measured_traffic(kernel_label, workload):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (already divided by the copy calibration), or None when
+    the record is for another workload or the kernel source has changed since
+    the counters were taken."""
+    import hashlib
+    if workload != DEFAULT or not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = json.load(open(TRAFFIC_RECORD))
+    k = rec.get("kernels", {}).get(KERNEL_KEYS.get(kernel_label, ""))
+    if not k:
+        return None
+    h = hashlib.sha256()
+    for f in k["source_files"]:
+        h.update(open(os.path.join(ROOT, "exact_tiled_attention_09_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != k["source_sha256"]:
+        return None
+    return int(k["hbm_read_bytes"] + k["hbm_write_bytes"])
+
+
 def cpu_baseline(inp, cfg, scale):
     """The fp64 oracle on one (b, h) head, forward + backward, scaled to the
     whole batch (B*H heads): a reported baseline, not a target."""
@@ -218,7 +244,8 @@ def main(argv=None):
                 "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2)},
         "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom, args.workload),
                      "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)},
         "cpu_baseline": None,
     }

@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows)
 
 // ---------------------------------------------------------------- kernel 2
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktiles) {
   constexpr int NW = 4;
   constexpr int BK = NW * 32;        // keys per workgroup
   constexpr int BQ = 64;             // query rows per step
@@ -86,9 +86,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];          // LSE * log2(e), +inf if dead
   __shared__ __attribute__((aligned(16))) float sDv[2][BQ];         // D
 
-  const int nbh = a.B * a.H;
-  const int bh = blockIdx.x % nbh;
-  const int kt = blockIdx.x / nbh;  // key tiles in order: the earliest carry the most work
+  int bh, kt;
+  wg_coords(blockIdx.x, a.B * a.H, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const SeqView sv = seq_view<VARLEN>(a, b, h, D);
@@ -96,7 +95,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a) {
   if (k0 >= sv.len) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -235,6 +234,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a) {
           s = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks])), s);
           dp = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks])), dp);
         }
+        float cc = c;
+        if (need_mask) {
+          // Masked entries get an exponent argument of -inf (exp2 -> 0); the
+          // scale is applied before the select and the exponent then uses
+          // multiplier 1, so a zero or negative scale cannot make 0 * -inf.
+          cc = 1.f;
+          const int key_m = pin_in_branch(key_ok ? my_key : 0x7fffffff);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            bool vis = key_m != 0x7fffffff;
+            if (CAUSAL) vis = vis && (key_m <= q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3));
+            s[r] = vis ? s[r] * c : kNegInf;
+          }
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + g * 8 + hi * 4;
@@ -243,12 +256,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = g * 4 + e;
-            float p = fast_exp2(__builtin_fmaf(s[r], c, -lv[e]));
-            if (need_mask) {
-              bool vis = key_ok;
-              if (CAUSAL) vis = vis && (my_key <= q0 + ql + e);
-              p = vis ? p : 0.f;
-            }
+            const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lv[e]));
             s[r] = p;
             dp[r] = p * (dp[r] - dvv[e]);
           }
@@ -315,10 +323,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   __shared__ uint8_t s_valid[2][BC];
   __shared__ uint32_t s_anypad[2];
 
-  const int nbh = a.B * a.H;
-  const int bh = blockIdx.x % nbh;
-  int tile = blockIdx.x / nbh;
-  if (CAUSAL) tile = n_qtiles - 1 - tile;  // heaviest query tiles first
+  int bh, tile;
+  wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);  // causal: heaviest first
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const SeqView sv = seq_view<VARLEN>(a, b, h, D);
@@ -326,7 +332,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   if (q_tile0 >= sv.len) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -455,17 +461,25 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
           s = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s);
           dp = mfma_bf16(as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks])), gf[ks], dp);
         }
+        float cc = c;
+        if (need_mask) {
+          // Masked entries get an exponent argument of -inf (exp2 -> 0),
+          // with the scale applied before the select (see the key-tile pass).
+          cc = 1.f;
+          const int q_m = pin_in_branch(qi);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) {
             const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
             const int key = kt0 + kl;
             bool vis = key < kv_len;
-            if (CAUSAL) vis = vis && key <= qi;
+            if (CAUSAL) vis = vis && key <= q_m;
             if (KPAD) vis = vis && s_valid[buf][kl] != 0;
-            p = vis ? p : 0.f;
+            s[r] = vis ? s[r] * c : kNegInf;
           }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lse2));
           dp[r] = p * (dp[r] - dd);
         }
         // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read.
@@ -528,7 +542,8 @@ static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)((a.N + BK - 1) / BK) * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                     (a.N + BK - 1) / BK);
   return hipGetLastError();
 }
 

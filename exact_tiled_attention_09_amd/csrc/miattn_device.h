@@ -90,6 +90,34 @@ __device__ __forceinline__ SeqView seq_view(const AttnArgs& a, int b, int h, int
   return s;
 }
 
+// Workgroup -> (sequence*head, tile), tile-major: every head's tile t before any
+// head's tile t+1 (with heavy_last_tile, the last tile first), so the
+// heaviest tiles of all heads start first and the grid ends on light ones.
+// Consecutive workgroups of one head land on one XCD when the head count is a
+// multiple of 8.
+__device__ __forceinline__ void wg_coords_tile_major(int w, int nbh, int ntile, bool heavy_last_tile, int& bh,
+                                                     int& t) {
+  bh = w % nbh;
+  t = w / nbh;
+  if (heavy_last_tile) t = ntile - 1 - t;
+}
+
+// Workgroup -> (sequence*head, tile).  Workgroups are dispatched to the 8 XCDs
+// in turn (w -> XCD w % 8), each XCD with its own L2.  When the grid divides by
+// 8, XCD x takes the contiguous logical range [x*total/8, (x+1)*total/8),
+// ordered head-major, so an XCD works through one or two heads at a time with
+// all of their tiles in flight and their K/V (or Q/dO) stays in its L2.
+// Otherwise the plain head-major order is used.  `heavy_last_tile` reverses
+// the tile order inside a head when the last tile carries the most work.
+__device__ __forceinline__ void wg_coords(int w, int nbh, int ntile, bool heavy_last_tile, int& bh, int& t) {
+  const int total = nbh * ntile;
+  int g = w;
+  if ((total & 7) == 0) g = (w & 7) * (total >> 3) + (w >> 3);
+  bh = g / ntile;
+  t = g - bh * ntile;
+  if (heavy_last_tile) t = ntile - 1 - t;
+}
+
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -164,6 +192,33 @@ __device__ __forceinline__ int swz_off(int r, int col) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: conditions derived from it then compile to scalar branches instead
+// of per-lane predication.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Masking and rescaling run only on a few tiles (diagonal, sequence end,
+// padded keys, a moved row max), behind wave-uniform branches.  The compiler
+// otherwise hoists their side-effect-free arithmetic above the branch and
+// pays for it on every tile.  Passing an input of that arithmetic through an
+// empty volatile asm inside the branch pins the computation there.
+template <typename T>
+__device__ __forceinline__ T pin_in_branch(T x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// Direct 16-byte global -> LDS load (global_load_lds_dwordx4): lane i of the
+// wave writes its 16 bytes to lds_wave_base + 16 * i.  lds_wave_base must be
+// wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (MIATTN_LDS void*)(lds_wave_base), 16, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including the
+// direct-to-LDS loads) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
