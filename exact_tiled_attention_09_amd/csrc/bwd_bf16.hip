@@ -30,6 +30,8 @@
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
+#include <cstdlib>
+
 namespace miattn {
 
 // ---------------------------------------------------------------- kernel 1
@@ -68,23 +70,34 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows)
 }
 
 // ---------------------------------------------------------------- kernel 2
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktiles) {
-  constexpr int NW = 4;
-  constexpr int BK = NW * 32;        // keys per workgroup
+// NW = 4: each wave owns 32 keys and both 32-row halves of every query tile.
+// NW = 8: waves w and w+4 own the same 32 keys and split the query tile by
+// halves, two waves per SIMD; their partial dK/dV are summed through LDS at
+// the end.
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
+__global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktiles) {
+  constexpr int NT = NW * 64;
+  constexpr int BK = 128;            // keys per workgroup (4 blocks of 32)
   constexpr int BQ = 64;             // query rows per step
   constexpr int KS = D / 16;         // k-steps over the head dim
   constexpr int DB = D / 32;
   constexpr int CH_PER_ROW = D / 8;
-  constexpr int QCPT = BQ * CH_PER_ROW / 256;  // 16-byte chunks per thread, Q tile
-  constexpr int KCPT = BK * CH_PER_ROW / 256;
+  constexpr int QCPT = BQ * CH_PER_ROW / NT;  // 16-byte chunks per thread, Q tile
+  constexpr int KCPT = BK * CH_PER_ROW / NT;
+  constexpr int QHALVES = NW == 4 ? 2 : 1;     // query halves handled per wave
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BQ * D];   // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];          // LSE * log2(e), +inf if dead
-  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];         // D
+  // One LDS arena: K, V (resident), Q and dO (double-buffered); after the
+  // loop it is reused to sum the partial accumulators of the 8-wave form.
+  constexpr int KV_ELEMS = BK * D;
+  constexpr int QT_ELEMS = BQ * D;
+  __shared__ __attribute__((aligned(16))) uint16_t arena[2 * KV_ELEMS + 4 * QT_ELEMS];
+  uint16_t* const sK = arena;
+  uint16_t* const sV = arena + KV_ELEMS;
+  uint16_t* const sQb = arena + 2 * KV_ELEMS;              // [2][QT_ELEMS]
+  uint16_t* const sGb = arena + 2 * KV_ELEMS + 2 * QT_ELEMS; // [2][QT_ELEMS]
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // LSE * log2(e), +inf if dead
+  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];  // D
 
   int bh, kt;
   wg_coords(blockIdx.x, a.B * a.H, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
@@ -101,13 +114,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
   const int hi = lane >> 5;
   const int len = sv.len;
   const float c = a.scale_log2;
+  const int kblk = wave & 3;                 // which 32 keys
+  const int qh0 = NW == 4 ? 0 : (wave >> 2); // first query half handled
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
   const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
   const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
   const uint16_t* __restrict__ gp = (const uint16_t*)a.dout + sv.base;
 
-  const int wk0 = k0 + wave * 32;  // this wave's 32 keys
+  const int wk0 = k0 + kblk * 32;  // this wave's 32 keys
   const int my_key = wk0 + l32;
   bool key_ok = my_key < len;
   if constexpr (KPAD) {
@@ -118,7 +133,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
   // The workgroup's K and V tiles (rows past the sequence are zero).
 #pragma unroll
   for (int cidx = 0; cidx < KCPT; ++cidx) {
-    const int chunk = tid + cidx * 256;
+    const int chunk = tid + cidx * NT;
     const int row = chunk / CH_PER_ROW;
     const int col = (chunk - row * CH_PER_ROW) * 8;
     const int key = k0 + row;
@@ -145,7 +160,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
   int st_off[QCPT];
 #pragma unroll
   for (int cidx = 0; cidx < QCPT; ++cidx) {
-    const int chunk = tid + cidx * 256;
+    const int chunk = tid + cidx * NT;
     const int row = chunk / CH_PER_ROW;
     st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
   }
@@ -155,7 +170,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
     const int q0 = it * BQ;
 #pragma unroll
     for (int cidx = 0; cidx < QCPT; ++cidx) {
-      const int chunk = tid + cidx * 256;
+      const int chunk = tid + cidx * NT;
       const int row = chunk / CH_PER_ROW;
       const int col = (chunk - row * CH_PER_ROW) * 8;
       const int qi = q0 + row;
@@ -181,8 +196,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int cidx = 0; cidx < QCPT; ++cidx) {
-      *(u32x4*)(&sQ[buf][st_off[cidx]]) = rq[cidx];
-      *(u32x4*)(&sG[buf][st_off[cidx]]) = rg[cidx];
+      *(u32x4*)(sQb + buf * QT_ELEMS + st_off[cidx]) = rq[cidx];
+      *(u32x4*)(sGb + buf * QT_ELEMS + st_off[cidx]) = rg[cidx];
     }
     if (tid < BQ) {
       sL[buf][tid] = rl;
@@ -201,8 +216,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
   for (int R = 0; R < 2; ++R)
 #pragma unroll
     for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
-  const uint16_t* kb_rows = sK + wave * 32 * D;
-  const uint16_t* vb_rows = sV + wave * 32 * D;
+  const uint16_t* kb_rows = sK + kblk * 32 * D;
+  const uint16_t* vb_rows = sV + kblk * 32 * D;
 
   if (qt_begin < n_qt) {
     load_tile(qt_begin);
@@ -215,76 +230,95 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktil
     const int q0 = it * BQ;
     if (it + 1 < n_qt) load_tile(it + 1);
 
-    const bool live = !CAUSAL || (q0 + BQ - 1 >= wk0);
-    if (live) {
+    const uint16_t* q_s = sQb + buf * QT_ELEMS;
+    const uint16_t* g_s = sGb + buf * QT_ELEMS;
+#pragma unroll
+    for (int qq = 0; qq < QHALVES; ++qq) {
+      const int qb = qh0 + qq;
+      __builtin_amdgcn_sched_barrier(0);
+      if (CAUSAL && q0 + qb * 32 + 31 < wk0) continue;  // this half sees none of the wave's keys
       bool need_mask = (wk0 + 31 >= len) || any_bad_key;
-      if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0);
-      const uint16_t* q_s = sQ[buf];
-      const uint16_t* g_s = sG[buf];
-      // One 32-row half of the query tile at a time keeps S and dP to 32
-      // registers; the scheduling barriers stop the halves from interleaving.
+      if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0 + qb * 32);
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (CAUSAL && q0 + qb * 32 + 31 < wk0) continue;  // this half sees none of the wave's keys
-        f32x16 s = f32x16{}, dp = f32x16{};
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = qb * 32 * D + aoff[ks];
+        s = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks])), s);
+        dp = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks])), dp);
+      }
+      float cc = c;
+      if (need_mask) {
+        // Masked entries get an exponent argument of -inf (exp2 -> 0); the
+        // scale is applied before the select and the exponent then uses
+        // multiplier 1, so a zero or negative scale cannot make 0 * -inf.
+        cc = 1.f;
+        const int key_m = pin_in_branch(key_ok ? my_key : 0x7fffffff);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = qb * 32 * D + aoff[ks];
-          s = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks])), s);
-          dp = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks])), dp);
-        }
-        float cc = c;
-        if (need_mask) {
-          // Masked entries get an exponent argument of -inf (exp2 -> 0); the
-          // scale is applied before the select and the exponent then uses
-          // multiplier 1, so a zero or negative scale cannot make 0 * -inf.
-          cc = 1.f;
-          const int key_m = pin_in_branch(key_ok ? my_key : 0x7fffffff);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            bool vis = key_m != 0x7fffffff;
-            if (CAUSAL) vis = vis && (key_m <= q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3));
-            s[r] = vis ? s[r] * c : kNegInf;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = qb * 32 + g * 8 + hi * 4;
-          const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
-          const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = g * 4 + e;
-            const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lv[e]));
-            s[r] = p;
-            dp[r] = p * (dp[r] - dvv[e]);
-          }
-        }
-        // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA.
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 pa = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
-                                        s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
-          const bf16x8 da = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
-                                        dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-          const int rbase = (qb * 32 + 16 * t) * D;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 gb = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]),
-                                         lds_read_tr16(g_s + rbase + troff[1][db]));
-            const bf16x8 qbv = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]),
-                                          lds_read_tr16(q_s + rbase + troff[1][db]));
-            dv[db] = mfma_bf16(pa, gb, dv[db]);
-            dk[db] = mfma_bf16(da, qbv, dk[db]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          bool vis = key_m != 0x7fffffff;
+          if (CAUSAL) vis = vis && (key_m <= q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3));
+          s[r] = vis ? s[r] * c : kNegInf;
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = qb * 32 + g * 8 + hi * 4;
+        const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
+        const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = g * 4 + e;
+          const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lv[e]));
+          s[r] = p;
+          dp[r] = p * (dp[r] - dvv[e]);
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pa = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
+                                      s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
+        const bf16x8 da = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                                      dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
+        const int rbase = (qb * 32 + 16 * t) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 gb = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]),
+                                       lds_read_tr16(g_s + rbase + troff[1][db]));
+          const bf16x8 qbv = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]),
+                                        lds_read_tr16(q_s + rbase + troff[1][db]));
+          dv[db] = mfma_bf16(pa, gb, dv[db]);
+          dk[db] = mfma_bf16(da, qbv, dk[db]);
+        }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     if (it + 1 < n_qt) store_tile(buf ^ 1);
     __syncthreads();
+  }
+
+  if constexpr (NW == 8) {
+    // Waves 4-7 hand their partial sums to waves 0-3 (same keys) through LDS.
+    float* red = reinterpret_cast<float*>(arena);  // 4 waves x 2 x DB x 16 x 64 floats = 128 KiB at D = 128
+    if (wave >= 4) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red[(((kblk * 2 + 0) * DB + db) * 16 + r) * 64 + lane] = dk[db][r];
+          red[(((kblk * 2 + 1) * DB + db) * 16 + r) * 64 + lane] = dv[db][r];
+        }
+    }
+    __syncthreads();
+    if (wave >= 4) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[db][r] += red[(((kblk * 2 + 0) * DB + db) * 16 + r) * 64 + lane];
+        dv[db][r] += red[(((kblk * 2 + 1) * DB + db) * 16 + r) * 64 + lane];
+      }
   }
 
   // dK = scale * acc, dV = acc; accumulator rows are keys, columns features.
@@ -536,14 +570,27 @@ hipError_t launch_bwd_prep_bf16(const AttnArgs& a, int d, bool varlen, hipStream
   return hipGetLastError();
 }
 
+static int dkdv_waves() {
+  static int nw = [] {
+    const char* e = getenv("MIATTN_DKDV_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  return nw;
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
 static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BK = 128;
-  const int64_t blocks = (int64_t)((a.N + BK - 1) / BK) * a.B * a.H;
+  const int n_ktiles = (a.N + BK - 1) / BK;
+  const int64_t blocks = (int64_t)n_ktiles * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
-                     (a.N + BK - 1) / BK);
+  if (dkdv_waves() == 4)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                       n_ktiles);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(512), 0, stream, a,
+                       n_ktiles);
   return hipGetLastError();
 }
 
