@@ -130,23 +130,6 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   }
   const bool any_bad_key = wave_any(!key_ok);
 
-  // The workgroup's K and V tiles (rows past the sequence are zero).
-#pragma unroll
-  for (int cidx = 0; cidx < KCPT; ++cidx) {
-    const int chunk = tid + cidx * NT;
-    const int row = chunk / CH_PER_ROW;
-    const int col = (chunk - row * CH_PER_ROW) * 8;
-    const int key = k0 + row;
-    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-    if (key < len) {
-      xk = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
-      xv = *(const u32x4*)(vp + (int64_t)key * sv.tok_stride + col);
-    }
-    const int off = swz_off<D>(row, col);
-    *(u32x4*)(sK + off) = xk;
-    *(u32x4*)(sV + off) = xv;
-  }
-
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -157,53 +140,69 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   const int n_qt = (len + BQ - 1) / BQ;
   const int qt_begin = CAUSAL ? k0 / BQ : 0;
 
-  int st_off[QCPT];
+  // Q and dO tiles travel from global memory straight into LDS (direct
+  // loads; LDS chunk p = i*NT + tid of a tile holds row p / CH_PER_ROW, logical
+  // chunk (p % CH_PER_ROW) ^ swz(row)).  Rows past the sequence repeat its last
+  // row; their LSE entry is +inf, so P and dS vanish there.
+  int src_row[QCPT], src_col[QCPT];
 #pragma unroll
-  for (int cidx = 0; cidx < QCPT; ++cidx) {
-    const int chunk = tid + cidx * NT;
-    const int row = chunk / CH_PER_ROW;
-    st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
+  for (int i = 0; i < QCPT; ++i) {
+    const int pch = i * NT + tid;
+    const int row = pch / CH_PER_ROW;
+    src_row[i] = row;
+    src_col[i] = ((pch % CH_PER_ROW) ^ swz<D>(row)) << 3;
   }
-  u32x4 rq[QCPT], rg[QCPT];
-  float rl = 0.f, rd = 0.f;
-  auto load_tile = [&](int it) {
+  auto issue_tile = [&](int it, int buf) {
     const int q0 = it * BQ;
 #pragma unroll
-    for (int cidx = 0; cidx < QCPT; ++cidx) {
-      const int chunk = tid + cidx * NT;
-      const int row = chunk / CH_PER_ROW;
-      const int col = (chunk - row * CH_PER_ROW) * 8;
-      const int qi = q0 + row;
-      u32x4 xq = {0u, 0u, 0u, 0u}, xg = {0u, 0u, 0u, 0u};
-      if (qi < len) {
-        xq = *(const u32x4*)(qp + (int64_t)qi * sv.tok_stride + col);
-        xg = *(const u32x4*)(gp + (int64_t)qi * sv.tok_stride + col);
-      }
-      rq[cidx] = xq;
-      rg[cidx] = xg;
-    }
-    if (tid < BQ) {
-      const int qi = q0 + tid;
-      rl = kPosInf;
-      rd = 0.f;
-      if (qi < len) {
-        const float lse = a.lse[sv.row_base + qi];
-        rl = (lse == kNegInf) ? kPosInf : lse * kLog2e;
-        rd = a.dvec[sv.row_base + qi];
-      }
+    for (int i = 0; i < QCPT; ++i) {
+      const int64_t off = (int64_t)min(q0 + src_row[i], len - 1) * sv.tok_stride + src_col[i];
+      lds_dma16(qp + off, sQb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
+      lds_dma16(gp + off, sGb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int cidx = 0; cidx < QCPT; ++cidx) {
-      *(u32x4*)(sQb + buf * QT_ELEMS + st_off[cidx]) = rq[cidx];
-      *(u32x4*)(sGb + buf * QT_ELEMS + st_off[cidx]) = rg[cidx];
+  // LSE (as log2, +inf when the row is dead or past the end) and D of the
+  // tile's rows, through registers of the first BQ threads.
+  float rl = 0.f, rd = 0.f;
+  auto load_rows = [&](int it) {
+    if (tid < BQ) {
+      const int qi = it * BQ + tid;
+      const int qc = min(qi, len - 1);
+      const float lse = a.lse[sv.row_base + qc];
+      rl = (qi >= len || lse == kNegInf) ? kPosInf : lse * kLog2e;
+      rd = qi < len ? a.dvec[sv.row_base + qc] : 0.f;
     }
+  };
+  auto store_rows = [&](int buf) {
     if (tid < BQ) {
       sL[buf][tid] = rl;
       sDv[buf][tid] = rd;
     }
   };
+
+  // Prologue: the first Q/dO tile in flight, then K and V (rows past the
+  // sequence are zero) and the first LSE/D rows; one wait covers all.
+  if (qt_begin < n_qt) issue_tile(qt_begin, 0);
+#pragma unroll
+  for (int cidx = 0; cidx < KCPT; ++cidx) {
+    const int chunk = tid + cidx * NT;
+    const int row = chunk / CH_PER_ROW;
+    const int col = (chunk - row * CH_PER_ROW) * 8;
+    const int key = k0 + row;
+    const int kc = min(key, len - 1);
+    const uint32_t keep = key < len ? 0xffffffffu : 0u;
+    const u32x4 xk = *(const u32x4*)(kp + (int64_t)kc * sv.tok_stride + col) & keep;
+    const u32x4 xv = *(const u32x4*)(vp + (int64_t)kc * sv.tok_stride + col) & keep;
+    const int off = swz_off<D>(row, col);
+    *(u32x4*)(sK + off) = xk;
+    *(u32x4*)(sV + off) = xv;
+  }
+  if (qt_begin < n_qt) {
+    load_rows(qt_begin);
+    store_rows(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first Q/dO tile too
+  barrier_vmem_n<0>();
 
   // Per-lane operand offsets (a row's swizzle depends only on the row mod 16).
   int aoff[KS];       // b128 operand rows (query or key) l32, chunk 2*ks + hi
@@ -219,16 +218,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   const uint16_t* kb_rows = sK + kblk * 32 * D;
   const uint16_t* vb_rows = sV + kblk * 32 * D;
 
-  if (qt_begin < n_qt) {
-    load_tile(qt_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-
   for (int it = qt_begin; it < n_qt; ++it) {
     const int buf = (it - qt_begin) & 1;
     const int q0 = it * BQ;
-    if (it + 1 < n_qt) load_tile(it + 1);
+    if (it + 1 < n_qt) {
+      issue_tile(it + 1, buf ^ 1);
+      load_rows(it + 1);
+    }
 
     const uint16_t* q_s = sQb + buf * QT_ELEMS;
     const uint16_t* g_s = sGb + buf * QT_ELEMS;
@@ -294,8 +290,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    if (it + 1 < n_qt) store_tile(buf ^ 1);
-    __syncthreads();
+    if (it + 1 < n_qt) store_rows(buf ^ 1);
+    barrier_vmem_n<0>();  // the next tile has landed
   }
 
   if constexpr (NW == 8) {
@@ -341,6 +337,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
 }
 
 // ---------------------------------------------------------------- kernel 3
+// K and V tiles of 64 keys travel from global memory straight into LDS
+// (three buffers each, fetched two tiles ahead, as in the forward's
+// direct-load form); before the barrier that ends tile j each wave waits only
+// for its own loads of tile j+1.  Rows past the sequence repeat its last row
+// and are masked.
 template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qtiles) {
   constexpr int BC = 64;                 // keys per tile
@@ -349,13 +350,14 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   constexpr int DB = D / 32;
   constexpr int TILE = BC * D;
   constexpr int NT = NW * 64;
-  constexpr int CH_PER_ROW = D / 8;
-  constexpr int CPT = BC * CH_PER_ROW / NT;
-  static_assert(CPT * NT == BC * CH_PER_ROW, "tile chunks must divide evenly");
+  constexpr int CPR = D / 8;
+  constexpr int LPT = BC * CPR / NT;     // direct loads per thread per tensor and tile
+  static_assert(LPT * NT == BC * CPR, "tile chunks must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
-  __shared__ uint8_t s_valid[2][BC];
-  __shared__ uint32_t s_anypad[2];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
+  __shared__ uint8_t s_valid[3][BC];
+  __shared__ uint32_t s_anypad[3];
 
   int bh, tile;
   wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);  // causal: heaviest first
@@ -379,26 +381,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
   const uint16_t* __restrict__ gp = (const uint16_t*)a.dout + sv.base;
 
-  // Q and dO as B operands (lane = query, 8 features per k-step).
-  bf16x8 qf[KS], gf[KS];
   const bool row_ok = qi < sv.len;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-      x = *(const u32x4*)(qp + (int64_t)qi * sv.tok_stride + ks * 16 + hi * 8);
-      y = *(const u32x4*)(gp + (int64_t)qi * sv.tok_stride + ks * 16 + hi * 8);
-    }
-    qf[ks] = as_bf16x8(x);
-    gf[ks] = as_bf16x8(y);
-  }
-  float lse2 = kPosInf, dd = 0.f;  // a dead or out-of-range row gets P = 0
-  if (row_ok) {
-    const float lse = a.lse[sv.row_base + qi];
-    lse2 = (lse == kNegInf) ? kPosInf : lse * kLog2e;
-    dd = a.dvec[sv.row_base + qi];
-  }
-
+  bf16x8 qf[KS], gf[KS];  // loaded in the prologue
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
@@ -407,30 +391,27 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  int st_off[CPT];
+  int src_row[LPT], src_col[LPT];
 #pragma unroll
-  for (int cidx = 0; cidx < CPT; ++cidx) {
-    const int chunk = tid + cidx * NT;
-    const int row = chunk / CH_PER_ROW;
-    st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
+  for (int i = 0; i < LPT; ++i) {
+    const int pch = i * NT + tid;
+    const int row = pch / CPR;
+    src_row[i] = row;
+    src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
-  u32x4 rk[CPT], rv[CPT];
-  uint32_t rvalid = 1u;
-  auto load_tile = [&](int j) {
+  auto issue = [&](int j) {
+    uint16_t* dk_ = sK[j % 3];
+    uint16_t* dv_ = sV[j % 3];
 #pragma unroll
-    for (int cidx = 0; cidx < CPT; ++cidx) {
-      const int chunk = tid + cidx * NT;
-      const int row = chunk / CH_PER_ROW;
-      const int col = (chunk - row * CH_PER_ROW) * 8;
-      const int key = j * BC + row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < kv_len) {
-        zk = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
-        zv = *(const u32x4*)(vp + (int64_t)key * sv.tok_stride + col);
-      }
-      rk[cidx] = zk;
-      rv[cidx] = zv;
+    for (int i = 0; i < LPT; ++i) {
+      const int key = min(j * BC + src_row[i], kv_len - 1);
+      const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
+      lds_dma16(kp + off, dk_ + (i * NT + wave * 64) * 8);
+      lds_dma16(vp + off, dv_ + (i * NT + wave * 64) * 8);
     }
+  };
+  uint32_t rvalid = 1u;
+  auto load_flags = [&](int j) {
     if constexpr (KPAD) {
       if (wave == 0) {
         const int key = j * BC + lane;
@@ -438,19 +419,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
       }
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* sk = smem + buf * 2 * TILE;
-    uint16_t* sv_ = sk + TILE;
-#pragma unroll
-    for (int cidx = 0; cidx < CPT; ++cidx) {
-      *(u32x4*)(sk + st_off[cidx]) = rk[cidx];
-      *(u32x4*)(sv_ + st_off[cidx]) = rv[cidx];
-    }
+  auto store_flags = [&](int j) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        s_valid[buf][lane] = (uint8_t)rvalid;
+        s_valid[j % 3][lane] = (uint8_t)rvalid;
         const bool any = wave_any(rvalid == 0u);
-        if (lane == 0) s_anypad[buf] = any ? 1u : 0u;
+        if (lane == 0) s_anypad[j % 3] = any ? 1u : 0u;
       }
     }
   };
@@ -466,21 +440,48 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
 #pragma unroll
     for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  // Prologue: start tiles 0 and 1, then load this wave's Q, dO, LSE and D
+  // rows; one wait (which the compiler sees, so the loop waits for none of
+  // these loads again) covers all of them.
+  load_flags(0);
+  store_flags(0);
+  if (ntiles > 1) {
+    load_flags(1);
+    store_flags(1);
   }
-  __syncthreads();
+  issue(0);
+  if (ntiles > 1) issue(1);
+  // Q and dO as B operands (lane = query, 8 features per k-step).  Rows past
+  // the sequence load its last row and are zeroed (no branch).
+  const int qc = min(qi, sv.len - 1);
+  const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int64_t off = (int64_t)qc * sv.tok_stride + ks * 16 + hi * 8;
+    qf[ks] = as_bf16x8(*(const u32x4*)(qp + off) & keep);
+    gf[ks] = as_bf16x8(*(const u32x4*)(gp + off) & keep);
+  }
+  // a dead or out-of-range row gets P = 0
+  const float lse_raw = a.lse[sv.row_base + qc];
+  const float lse2 = (!row_ok || lse_raw == kNegInf) ? kPosInf : lse_raw * kLog2e;
+  const float dd = row_ok ? a.dvec[sv.row_base + qc] : 0.f;
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  barrier_vmem_n<0>();
 
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    const int buf = j % 3;
+    const bool fetch = j + 2 < ntiles;
+    if (fetch) {
+      load_flags(j + 2);
+      issue(j + 2);
+    }
 
     const int kt0 = j * BC;
     const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
     if (wave_live) {
-      const uint16_t* sk = smem + buf * 2 * TILE;
-      const uint16_t* svv = sk + TILE;
+      const uint16_t* sk = sK[buf];
+      const uint16_t* svv = sV[buf];
       bool need_mask = kt0 + BC > kv_len;
       if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
       if (KPAD) need_mask = need_mask || (s_anypad[buf] != 0u);
@@ -532,8 +533,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    if (fetch) store_flags(j + 2);
+    // this wave's loads of tile j + 1 have landed (those of j + 2 may not)
+    if (fetch) barrier_vmem_n<2 * LPT>();
+    else barrier_vmem_n<0>();
   }
 
   // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers = features).

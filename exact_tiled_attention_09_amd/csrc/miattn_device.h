@@ -210,15 +210,31 @@ __device__ __forceinline__ T pin_in_branch(T x) {
 }
 
 // Direct 16-byte global -> LDS load (global_load_lds_dwordx4): lane i of the
-// wave writes its 16 bytes to lds_wave_base + 16 * i.  lds_wave_base must be
-// wave-uniform.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (MIATTN_LDS void*)(lds_wave_base), 16, 0, 0);
+// wave writes its 16 bytes to lds_wave_base + 16 * i; lds_wave_base must be
+// wave-uniform (it goes to M0).  Issued through inline asm so that the
+// compiler does not track it: it then inserts no conservative waits for it
+// before unrelated LDS reads.  The caller orders it explicitly, with
+// barrier_vmem_n before any wave reads the destination, and only targets LDS
+// that no wave reads until that barrier.  M0 is written without being
+// declared (the compiler rejects clobbers of reserved registers); the kernels
+// keep no value of their own in M0.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MIATTN_LDS void*)lds_wave_base);
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
 }
 
-// Wait until this wave's outstanding vector-memory operations (including the
-// direct-to-LDS loads) have completed: s_waitcnt vmcnt(0).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier for kernels that keep direct-to-LDS loads in flight
+// across it.  __syncthreads() fences LDS, which makes the compiler wait for
+// every outstanding direct load (vmcnt(0)) first; here the wave waits until
+// at most N of its vector-memory operations (the N most recent, since they
+// complete in issue order) are outstanding and all of its LDS operations are
+// done, then meets the other waves.  The memory clobber keeps the compiler
+// from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void barrier_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt field of 4 bits used here");
+  __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
