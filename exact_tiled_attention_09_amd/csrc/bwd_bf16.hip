@@ -152,31 +152,38 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     src_row[i] = row;
     src_col[i] = ((pch % CH_PER_ROW) ^ swz<D>(row)) << 3;
   }
+  // Load number n (0 .. 2*QCPT-1) of this thread for tile it: Q for even n,
+  // dO for odd n, chunk n / 2.
+  auto issue_part = [&](int it, int buf, int n) {
+    const int i = n >> 1;
+    const int64_t off = (int64_t)min(it * BQ + src_row[i], len - 1) * sv.tok_stride + src_col[i];
+    if (n & 1) lds_dma16(gp + off, sGb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
+    else lds_dma16(qp + off, sQb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
+  };
   auto issue_tile = [&](int it, int buf) {
-    const int q0 = it * BQ;
 #pragma unroll
-    for (int i = 0; i < QCPT; ++i) {
-      const int64_t off = (int64_t)min(q0 + src_row[i], len - 1) * sv.tok_stride + src_col[i];
-      lds_dma16(qp + off, sQb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
-      lds_dma16(gp + off, sGb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
-    }
+    for (int n = 0; n < 2 * QCPT; ++n) issue_part(it, buf, n);
   };
   // LSE (as log2, +inf when the row is dead or past the end) and D of the
-  // tile's rows, through registers of the first BQ threads.
+  // tile's rows, through registers of wave 0 (BQ = 64 rows, one per lane).
+  // The raw values are loaded at the start of a step and converted only when
+  // stored at its end, so the wave does not wait for the loads in between.
+  static_assert(BQ == 64, "one row per lane of wave 0");
   float rl = 0.f, rd = 0.f;
+  int rq = 0;
   auto load_rows = [&](int it) {
-    if (tid < BQ) {
-      const int qi = it * BQ + tid;
-      const int qc = min(qi, len - 1);
-      const float lse = a.lse[sv.row_base + qc];
-      rl = (qi >= len || lse == kNegInf) ? kPosInf : lse * kLog2e;
-      rd = qi < len ? a.dvec[sv.row_base + qc] : 0.f;
+    if (wave == 0) {
+      rq = it * BQ + lane;
+      const int qc = min(rq, len - 1);
+      rl = a.lse[sv.row_base + qc];
+      rd = a.dvec[sv.row_base + qc];
     }
   };
   auto store_rows = [&](int buf) {
-    if (tid < BQ) {
-      sL[buf][tid] = rl;
-      sDv[buf][tid] = rd;
+    if (wave == 0) {
+      const bool out = rq >= len;
+      sL[buf][lane] = (out || rl == kNegInf) ? kPosInf : rl * kLog2e;
+      sDv[buf][lane] = out ? 0.f : rd;
     }
   };
 
@@ -221,10 +228,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   for (int it = qt_begin; it < n_qt; ++it) {
     const int buf = (it - qt_begin) & 1;
     const int q0 = it * BQ;
-    if (it + 1 < n_qt) {
-      issue_tile(it + 1, buf ^ 1);
-      load_rows(it + 1);
-    }
+    const bool fetch = it + 1 < n_qt;
+    if (fetch) load_rows(it + 1);
+    // The loads of tile it+1 are spread over the first live half's S / dP
+    // MFMAs (all waves issuing together would queue in the CU's memory
+    // pipeline); a wave with no live half issues them at once.
+    bool pending = fetch;
 
     const uint16_t* q_s = sQb + buf * QT_ELEMS;
     const uint16_t* g_s = sGb + buf * QT_ELEMS;
@@ -241,7 +250,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
         const int off = qb * 32 * D + aoff[ks];
         s = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks])), s);
         dp = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks])), dp);
+        if (pending) {
+#pragma unroll
+          for (int n = ks * 2 * QCPT / KS; n < (ks + 1) * 2 * QCPT / KS; ++n) issue_part(it + 1, buf ^ 1, n);
+        }
       }
+      pending = false;
       float cc = c;
       if (need_mask) {
         // Masked entries get an exponent argument of -inf (exp2 -> 0); the
@@ -290,7 +304,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    if (it + 1 < n_qt) store_rows(buf ^ 1);
+    if (pending) issue_tile(it + 1, buf ^ 1);
+    if (fetch) store_rows(buf ^ 1);
     barrier_vmem_n<0>();  // the next tile has landed
   }
 
@@ -399,31 +414,37 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     src_row[i] = row;
     src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
-  auto issue = [&](int j) {
-    uint16_t* dk_ = sK[j % 3];
-    uint16_t* dv_ = sV[j % 3];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int key = min(j * BC + src_row[i], kv_len - 1);
-      const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
-      lds_dma16(kp + off, dk_ + (i * NT + wave * 64) * 8);
-      lds_dma16(vp + off, dv_ + (i * NT + wave * 64) * 8);
-    }
+  // Load number n (0 .. 2*LPT-1) of this thread for tile j: K for even n, V
+  // for odd n, chunk n / 2.
+  auto issue_part = [&](int j, int n) {
+    const int i = n >> 1;
+    const int key = min(j * BC + src_row[i], kv_len - 1);
+    const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
+    if (n & 1) lds_dma16(vp + off, sV[j % 3] + (i * NT + wave * 64) * 8);
+    else lds_dma16(kp + off, sK[j % 3] + (i * NT + wave * 64) * 8);
   };
+  auto issue = [&](int j) {
+#pragma unroll
+    for (int n = 0; n < 2 * LPT; ++n) issue_part(j, n);
+  };
+  // Key-validity flags of a tile, by wave 0: the raw byte is loaded early
+  // and converted only when stored, so the wave does not wait in between.
   uint32_t rvalid = 1u;
+  int rkey = 0;
   auto load_flags = [&](int j) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        const int key = j * BC + lane;
-        rvalid = (key < kv_len) ? (uint32_t)(a.key_valid[sv.tok0 + key] != 0) : 1u;
+        rkey = j * BC + lane;
+        rvalid = a.key_valid[sv.tok0 + min(rkey, kv_len - 1)];
       }
     }
   };
   auto store_flags = [&](int j) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        s_valid[j % 3][lane] = (uint8_t)rvalid;
-        const bool any = wave_any(rvalid == 0u);
+        const uint32_t ok = (rkey >= kv_len || rvalid != 0u) ? 1u : 0u;  // keys past the end are masked anyway
+        s_valid[j % 3][lane] = (uint8_t)ok;
+        const bool any = wave_any(ok == 0u);
         if (lane == 0) s_anypad[j % 3] = any ? 1u : 0u;
       }
     }
@@ -472,13 +493,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j % 3;
     const bool fetch = j + 2 < ntiles;
-    if (fetch) {
-      load_flags(j + 2);
-      issue(j + 2);
-    }
-
     const int kt0 = j * BC;
     const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
+    if (fetch) load_flags(j + 2);
+    // A wave with work spreads its loads of tile j+2 over the first block's
+    // S^T / dP^T MFMAs; an idle wave issues them at once.
+    if (fetch && !wave_live) issue(j + 2);
     if (wave_live) {
       const uint16_t* sk = sK[buf];
       const uint16_t* svv = sV[buf];
@@ -495,6 +515,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
         for (int ks = 0; ks < KS; ++ks) {
           s = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s);
           dp = mfma_bf16(as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks])), gf[ks], dp);
+          if (kb == 0 && fetch) {  // block 0 is never skipped when the wave is live
+#pragma unroll
+            for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + 2, n);
+          }
         }
         float cc = c;
         if (need_mask) {

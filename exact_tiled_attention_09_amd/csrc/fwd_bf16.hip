@@ -657,31 +657,38 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
     src_row[i] = row;
     src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
+  // Load number n (0 .. 2*LPT-1) of this thread for tile j: K for even n, V
+  // for odd n, chunk n / 2.
+  auto issue_part = [&](uint16_t* sk, uint16_t* svv, int j, int n) {
+    const int i = n >> 1;
+    const int key = min(j * BC + src_row[i], kv_len - 1);
+    const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
+    if (n & 1) lds_dma16(vp + off, svv + (i * NT + wave * 64) * 8);
+    else lds_dma16(kp + off, sk + (i * NT + wave * 64) * 8);
+  };
   auto issue = [&](uint16_t* sk, uint16_t* svv, int j) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int key = min(j * BC + src_row[i], kv_len - 1);
-      const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
-      lds_dma16(kp + off, sk + (i * NT + wave * 64) * 8);
-      lds_dma16(vp + off, svv + (i * NT + wave * 64) * 8);
-    }
+    for (int n = 0; n < 2 * LPT; ++n) issue_part(sk, svv, j, n);
   };
-  // Key-validity flags of a tile, by wave 0: loaded before the tile's direct
-  // loads are issued and stored at the end of the step.
+  // Key-validity flags of a tile, by wave 0: the raw byte is loaded before
+  // the tile's direct loads are issued and converted only when stored at the
+  // end of the step, so the wave does not wait in between.
   uint32_t rvalid = 1u;
+  int rkey = 0;
   auto load_flags = [&](int j) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        const int key = j * BC + lane;
-        rvalid = (key < kv_len) ? (uint32_t)(a.key_valid[sv.tok0 + key] != 0) : 1u;
+        rkey = j * BC + lane;
+        rvalid = a.key_valid[sv.tok0 + min(rkey, kv_len - 1)];
       }
     }
   };
   auto store_flags = [&](int slot) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        s_valid[slot][lane] = (uint8_t)rvalid;
-        const bool any = wave_any(rvalid == 0u);
+        const uint32_t ok = (rkey >= kv_len || rvalid != 0u) ? 1u : 0u;  // keys past the end are masked anyway
+        s_valid[slot][lane] = (uint8_t)ok;
+        const bool any = wave_any(ok == 0u);
         if (lane == 0) s_anypad[slot] = any ? 1u : 0u;
       }
     }
@@ -702,21 +709,27 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
   // O^T += V^T P^T; j + 2 is fetched into slot (B + 2) % 3 meanwhile.
   auto step = [&](int j, uint16_t* sk, uint16_t* svt, uint16_t* nk, uint16_t* nv, int slot, int nslot) {
     const bool fetch = j + 2 < ntiles;
-    if (fetch) {
-      load_flags(j + 2);
-      issue(nk, nv, j + 2);
-    }
     const int kt0 = j * BC;
     const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
+    if (fetch) load_flags(j + 2);
+    // A wave with work spreads its loads of tile j+2 over the S^T MFMAs (all
+    // waves issuing together would queue in the CU's memory pipeline); an idle
+    // wave issues them at once.
+    if (fetch && !wave_live) issue(nk, nv, j + 2);
     if (wave_live) {
       f32x16 s[2];
       s[0] = f32x16{};
       s[1] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           s[kb] = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s[kb]);
+        if (fetch) {
+#pragma unroll
+          for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(nk, nv, j + 2, n);
+        }
+      }
 
       bool need_mask = kt0 + BC > kv_len;
       if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);

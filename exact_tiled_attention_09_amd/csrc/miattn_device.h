@@ -212,15 +212,17 @@ __device__ __forceinline__ T pin_in_branch(T x) {
 // Direct 16-byte global -> LDS load (global_load_lds_dwordx4): lane i of the
 // wave writes its 16 bytes to lds_wave_base + 16 * i; lds_wave_base must be
 // wave-uniform (it goes to M0).  Issued through inline asm so that the
-// compiler does not track it: it then inserts no conservative waits for it
-// before unrelated LDS reads.  The caller orders it explicitly, with
-// barrier_vmem_n before any wave reads the destination, and only targets LDS
-// that no wave reads until that barrier.  M0 is written without being
-// declared (the compiler rejects clobbers of reserved registers); the kernels
-// keep no value of their own in M0.
+// compiler does not track it: it inserts no conservative waits for it before
+// unrelated LDS reads, and (no memory clobber) it may schedule LDS reads and
+// MFMAs across it, which lets the kernels spread their loads between MFMAs.
+// Contract for callers: the destination is LDS that no wave reads before the
+// next barrier_vmem_n, and that barrier waits for the load.  Both are volatile
+// asm, so the compiler keeps them in program order.  M0 is written without
+// being declared (the compiler rejects clobbers of reserved registers); the
+// kernels keep no value of their own in M0.
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MIATTN_LDS void*)lds_wave_base);
-  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m));
 }
 
 // Workgroup barrier for kernels that keep direct-to-LDS loads in flight
