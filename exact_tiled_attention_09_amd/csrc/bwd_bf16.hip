@@ -31,6 +31,7 @@
 #include "miattn_launch.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace miattn {
 
@@ -87,15 +88,17 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   constexpr int QHALVES = NW == 4 ? 2 : 1;     // query halves handled per wave
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
 
-  // One LDS arena: K, V (resident), Q and dO (double-buffered); after the
-  // loop it is reused to sum the partial accumulators of the 8-wave form.
+  // One LDS arena: Q and dO (double-buffered), then K and V (resident);
+  // after the loop it is reused to sum the partial accumulators of the
+  // 8-wave form.  The per-step Q/dO buffers come first so that, at D = 128,
+  // every one of their offsets fits the 16-bit immediate of an LDS read.
   constexpr int KV_ELEMS = BK * D;
   constexpr int QT_ELEMS = BQ * D;
   __shared__ __attribute__((aligned(16))) uint16_t arena[2 * KV_ELEMS + 4 * QT_ELEMS];
-  uint16_t* const sK = arena;
-  uint16_t* const sV = arena + KV_ELEMS;
-  uint16_t* const sQb = arena + 2 * KV_ELEMS;              // [2][QT_ELEMS]
-  uint16_t* const sGb = arena + 2 * KV_ELEMS + 2 * QT_ELEMS; // [2][QT_ELEMS]
+  uint16_t* const sQb = arena;                              // [2][QT_ELEMS]
+  uint16_t* const sGb = arena + 2 * QT_ELEMS;               // [2][QT_ELEMS]
+  uint16_t* const sK = arena + 4 * QT_ELEMS;
+  uint16_t* const sV = arena + 4 * QT_ELEMS + KV_ELEMS;
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // LSE * log2(e), +inf if dead
   __shared__ __attribute__((aligned(16))) float sDv[2][BQ];  // D
 
@@ -225,8 +228,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   const uint16_t* kb_rows = sK + kblk * 32 * D;
   const uint16_t* vb_rows = sV + kblk * 32 * D;
 
-  for (int it = qt_begin; it < n_qt; ++it) {
-    const int buf = (it - qt_begin) & 1;
+  // One query tile from buffer BUF (= (it - qt_begin) % 2, a compile-time
+  // constant so that every LDS address is a register plus an immediate).
+  auto step = [&](int it, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int q0 = it * BQ;
     const bool fetch = it + 1 < n_qt;
     if (fetch) load_rows(it + 1);
@@ -307,6 +312,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     if (pending) issue_tile(it + 1, buf ^ 1);
     if (fetch) store_rows(buf ^ 1);
     barrier_vmem_n<0>();  // the next tile has landed
+  };
+  for (int it = qt_begin; it < n_qt; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   if constexpr (NW == 8) {
@@ -490,8 +499,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   barrier_vmem_n<0>();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j % 3;
+  // One key tile from buffer slot BUF (= j % 3, a compile-time constant).
+  auto step = [&](int j, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const bool fetch = j + 2 < ntiles;
     const int kt0 = j * BC;
     const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
@@ -561,6 +571,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     // this wave's loads of tile j + 1 have landed (those of j + 2 may not)
     if (fetch) barrier_vmem_n<2 * LPT>();
     else barrier_vmem_n<0>();
+  };
+  for (int j = 0; j < ntiles; j += 3) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
   }
 
   // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers = features).

@@ -34,6 +34,7 @@
 #include "miattn_launch.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace miattn {
 
@@ -586,15 +587,17 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
 // Direct-load form (the default).  Same per-wave work as fwd_bf16_kernel
 // with one 32-row block per wave, but K and V tiles travel from global memory
 // straight into LDS (global_load_lds_dwordx4: no register staging and no LDS
-// stores) two tiles ahead, through three buffers per tensor.  Before the
+// stores) NBUF - 1 tiles ahead, through NBUF buffers per tensor.  Before the
 // barrier that ends tile j, each wave waits only for its own loads of tile
-// j+1, so a load has two tiles of compute to land.  The key loop is unrolled
-// by three so that every buffer address is a compile-time constant.  Rows past
-// the end of the sequence are loaded from its last row (finite values) and
-// masked.
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtiles) {
-  constexpr int NW = 8;
+// j+1, so a load has NBUF - 1 tiles of compute to land.  The key loop is
+// unrolled by NBUF so that every buffer address is a compile-time constant.
+// Rows past the end of the sequence are loaded from its last row (finite
+// values) and masked.  NW = 8 runs one workgroup of 256 rows per CU; NW = 4
+// with two buffers runs two independent workgroups of 128 rows per CU, each
+// with its own barrier, so the two waves that share a SIMD are not held in
+// step by a common barrier.
+template <int D, int NW, int NBUF, bool CAUSAL, bool VARLEN, bool KPAD>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, int n_qtiles) {
   constexpr int BC = 64;
   constexpr int BR = NW * 32;
   constexpr int KS = D / 16;
@@ -603,16 +606,15 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int LPT = BC * CPR / NT;     // direct loads per thread per tensor and tile
+  constexpr int AHEAD = NBUF - 1;        // tiles in flight ahead of the one in use
   static_assert(LPT * NT == BC * CPR, "tile chunks must divide evenly");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
+  static_assert(AHEAD * 2 * LPT < 16, "vmcnt field of 4 bits");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sK2[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV2[TILE];
-  __shared__ uint8_t s_valid[3][BC];
-  __shared__ uint32_t s_anypad[3];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
+  __shared__ uint8_t s_valid[NBUF][BC];
+  __shared__ uint32_t s_anypad[NBUF];
 
   int bh, tile;
   wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);  // causal: heaviest first
@@ -659,16 +661,16 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
   }
   // Load number n (0 .. 2*LPT-1) of this thread for tile j: K for even n, V
   // for odd n, chunk n / 2.
-  auto issue_part = [&](uint16_t* sk, uint16_t* svv, int j, int n) {
+  auto issue_part = [&](int j, int n) {
     const int i = n >> 1;
     const int key = min(j * BC + src_row[i], kv_len - 1);
     const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
-    if (n & 1) lds_dma16(vp + off, svv + (i * NT + wave * 64) * 8);
-    else lds_dma16(kp + off, sk + (i * NT + wave * 64) * 8);
+    if (n & 1) lds_dma16(vp + off, sV[j % NBUF] + (i * NT + wave * 64) * 8);
+    else lds_dma16(kp + off, sK[j % NBUF] + (i * NT + wave * 64) * 8);
   };
-  auto issue = [&](uint16_t* sk, uint16_t* svv, int j) {
+  auto issue = [&](int j) {
 #pragma unroll
-    for (int n = 0; n < 2 * LPT; ++n) issue_part(sk, svv, j, n);
+    for (int n = 0; n < 2 * LPT; ++n) issue_part(j, n);
   };
   // Key-validity flags of a tile, by wave 0: the raw byte is loaded before
   // the tile's direct loads are issued and converted only when stored at the
@@ -705,17 +707,21 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
 #pragma unroll
     for (int db = 0; db < DB; ++db) voff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
 
-  // One key tile from buffer slot B: S^T = K Q^T, mask, online softmax,
-  // O^T += V^T P^T; j + 2 is fetched into slot (B + 2) % 3 meanwhile.
-  auto step = [&](int j, uint16_t* sk, uint16_t* svt, uint16_t* nk, uint16_t* nv, int slot, int nslot) {
-    const bool fetch = j + 2 < ntiles;
+  // One key tile from buffer slot U (= j % NBUF): S^T = K Q^T, mask, online
+  // softmax, O^T += V^T P^T; tile j + AHEAD is fetched meanwhile.
+  auto step = [&](int j, auto slot_c) {
+    constexpr int U = decltype(slot_c)::value;
+    constexpr int NU = (U + AHEAD) % NBUF;
+    const uint16_t* sk = sK[U];
+    const uint16_t* svt = sV[U];
+    const bool fetch = j + AHEAD < ntiles;
     const int kt0 = j * BC;
     const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
-    if (fetch) load_flags(j + 2);
-    // A wave with work spreads its loads of tile j+2 over the S^T MFMAs (all
-    // waves issuing together would queue in the CU's memory pipeline); an idle
-    // wave issues them at once.
-    if (fetch && !wave_live) issue(nk, nv, j + 2);
+    if (fetch) load_flags(j + AHEAD);
+    // A wave with work spreads its loads of tile j+AHEAD over the S^T MFMAs
+    // (all waves issuing together would queue in the CU's memory pipeline);
+    // an idle wave issues them at once.
+    if (fetch && !wave_live) issue(j + AHEAD);
     if (wave_live) {
       f32x16 s[2];
       s[0] = f32x16{};
@@ -727,13 +733,13 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
           s[kb] = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s[kb]);
         if (fetch) {
 #pragma unroll
-          for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(nk, nv, j + 2, n);
+          for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + AHEAD, n);
         }
       }
 
       bool need_mask = kt0 + BC > kv_len;
       if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
-      if (KPAD) need_mask = need_mask || (s_anypad[slot] != 0u);
+      if (KPAD) need_mask = need_mask || (s_anypad[U] != 0u);
       float cc = c;
       if (need_mask) {
         // Scale first, then hide masked entries as -inf; afterwards the
@@ -748,7 +754,7 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
             const int key = kt0 + kl;
             bool vis = key < kv_len;
             if (CAUSAL) vis = vis && key <= qi;
-            if (KPAD) vis = vis && s_valid[slot][kl] != 0;
+            if (KPAD) vis = vis && s_valid[U][kl] != 0;
             s[kb][r] = vis ? s[kb][r] * c : kNegInf;
           }
       }
@@ -795,23 +801,28 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
           }
         }
     }
-    if (fetch) store_flags(nslot);
-    // this wave's loads of tile j + 1 have landed (those of j + 2 may not)
-    if (fetch) barrier_vmem_n<2 * LPT>();
-    else barrier_vmem_n<0>();
+    if (fetch) store_flags(NU);
+    // this wave's loads of tile j + 1 have landed (those issued after them,
+    // for tiles j + 2 .. j + AHEAD, may not have)
+    if constexpr (AHEAD == 2) {
+      if (fetch) barrier_vmem_n<2 * LPT>();
+      else barrier_vmem_n<0>();
+    } else {
+      barrier_vmem_n<0>();
+    }
   };
 
-  // Prologue: start tiles 0 and 1, then load this wave's Q rows; one wait
-  // (which the compiler sees, so the loop waits for none of these loads
+  // Prologue: start tiles 0 .. AHEAD-1, then load this wave's Q rows; one
+  // wait (which the compiler sees, so the loop waits for none of these loads
   // again) covers all of them.
-  load_flags(0);
-  store_flags(0);
-  if (ntiles > 1) {
-    load_flags(1);
-    store_flags(1);
+#pragma unroll
+  for (int t = 0; t < AHEAD; ++t) {
+    if (t < ntiles) {
+      load_flags(t);
+      store_flags(t);
+      issue(t);
+    }
   }
-  issue(sK0, sV0, 0);
-  if (ntiles > 1) issue(sK1, sV1, 1);
   {
     // rows past the sequence load its last row and are zeroed (no branch)
     const int qi = q_wave0 + l32;
@@ -822,10 +833,12 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   barrier_vmem_n<0>();
-  for (int j = 0; j < ntiles; j += 3) {
-    step(j, sK0, sV0, sK2, sV2, 0, 2);
-    if (j + 1 < ntiles) step(j + 1, sK1, sV1, sK0, sV0, 1, 0);
-    if (j + 2 < ntiles) step(j + 2, sK2, sV2, sK1, sV1, 2, 1);
+  for (int j = 0; j < ntiles; j += NBUF) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
+    if constexpr (NBUF == 3) {
+      if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   // Epilogue: O = O~ / l, LSE = ln 2 * (m + log2 l); a row that saw no
@@ -849,25 +862,28 @@ __global__ void __launch_bounds__(512, 1) fwd_dma_kernel(AttnArgs a, int n_qtile
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
+template <int D, int NW, int NBUF, bool CAUSAL, bool VARLEN, bool KPAD>
 static hipError_t launch_fwd_dma_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int BR = 8 * 32;
+  constexpr int BR = NW * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_dma_kernel<D, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(512), 0, stream, a,
-                     n_qtiles);
+  hipLaunchKernelGGL((fwd_dma_kernel<D, NW, NBUF, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     stream, a, n_qtiles);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int NW, int NBUF>
 static hipError_t dispatch_fwd_dma(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
   if (varlen) {
-    if (causal) return kpad ? launch_fwd_dma_t<D, true, true, true>(a, s) : launch_fwd_dma_t<D, true, true, false>(a, s);
-    return kpad ? launch_fwd_dma_t<D, false, true, true>(a, s) : launch_fwd_dma_t<D, false, true, false>(a, s);
+    if (causal) return kpad ? launch_fwd_dma_t<D, NW, NBUF, true, true, true>(a, s)
+                            : launch_fwd_dma_t<D, NW, NBUF, true, true, false>(a, s);
+    return kpad ? launch_fwd_dma_t<D, NW, NBUF, false, true, true>(a, s)
+                : launch_fwd_dma_t<D, NW, NBUF, false, true, false>(a, s);
   }
-  return causal ? launch_fwd_dma_t<D, true, false, false>(a, s) : launch_fwd_dma_t<D, false, false, false>(a, s);
+  return causal ? launch_fwd_dma_t<D, NW, NBUF, true, false, false>(a, s)
+                : launch_fwd_dma_t<D, NW, NBUF, false, false, false>(a, s);
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE>
@@ -937,13 +953,15 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, h
     if (t == 1) return dispatch_fwd_stag<128, 0>(a, causal, varlen, kpad, stream);
     if (t == 2) return dispatch_fwd_stag<128, 1>(a, causal, varlen, kpad, stream);
     if (t == 3) return dispatch_fwd<128, 1, 8, 1>(a, causal, varlen, kpad, stream);
-    return dispatch_fwd_dma<128>(a, causal, varlen, kpad, stream);
+    if (t == 5) return dispatch_fwd_dma<128, 4, 2>(a, causal, varlen, kpad, stream);
+    return dispatch_fwd_dma<128, 8, 3>(a, causal, varlen, kpad, stream);
   }
   if (d == 64) {
     if (t == 1) return dispatch_fwd_stag<64, 0>(a, causal, varlen, kpad, stream);
     if (t == 2) return dispatch_fwd_stag<64, 1>(a, causal, varlen, kpad, stream);
     if (t == 3) return dispatch_fwd<64, 1, 8, 1>(a, causal, varlen, kpad, stream);
-    return dispatch_fwd_dma<64>(a, causal, varlen, kpad, stream);
+    if (t == 5) return dispatch_fwd_dma<64, 4, 2>(a, causal, varlen, kpad, stream);
+    return dispatch_fwd_dma<64, 8, 3>(a, causal, varlen, kpad, stream);
   }
   return hipErrorInvalidValue;
 }
