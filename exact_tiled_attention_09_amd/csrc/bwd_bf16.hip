@@ -249,16 +249,27 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
       if (CAUSAL && q0 + qb * 32 + 31 < wk0) continue;  // this half sees none of the wave's keys
       bool need_mask = (wk0 + 31 >= len) || any_bad_key;
       if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0 + qb * 32);
+      // S and dP, their four operands read one k-step ahead.
       f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 opq[2], opk[2], opg[2], opv[2];
+      auto sread = [&](int ks, int u) __attribute__((always_inline)) {
+        const int off = qb * 32 * D + aoff[ks];
+        opq[u] = as_bf16x8(*(const u32x4*)(q_s + off));
+        opk[u] = as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks]));
+        opg[u] = as_bf16x8(*(const u32x4*)(g_s + off));
+        opv[u] = as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks]));
+      };
+      sread(0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = qb * 32 * D + aoff[ks];
-        s = mfma_bf16(as_bf16x8(*(const u32x4*)(q_s + off)), as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks])), s);
-        dp = mfma_bf16(as_bf16x8(*(const u32x4*)(g_s + off)), as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks])), dp);
+        if (ks + 1 < KS) sread(ks + 1, (ks + 1) & 1);
+        s = mfma_bf16(opq[ks & 1], opk[ks & 1], s);
+        dp = mfma_bf16(opg[ks & 1], opv[ks & 1], dp);
         if (pending) {
 #pragma unroll
           for (int n = ks * 2 * QCPT / KS; n < (ks + 1) * 2 * QCPT / KS; ++n) issue_part(it + 1, buf ^ 1, n);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       pending = false;
       float cc = c;
@@ -288,23 +299,31 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
           dp[r] = p * (dp[r] - dvv[e]);
         }
       }
-      // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA.
+      // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA; the
+      // transposed dO / Q operands are read one MFMA pair ahead.
+      bf16x8 pa[2], da[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 pa = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
-                                      s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
-        const bf16x8 da = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
-                                      dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-        const int rbase = (qb * 32 + 16 * t) * D;
+        pa[t] = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
+                            s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
+        da[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                            dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
+      }
+      constexpr int NKK = 2 * DB;  // (t, db) pairs
+      bf16x8 opgt[2], opqt[2];
+      auto tread = [&](int i, int u) __attribute__((always_inline)) {
+        const int rbase = (qb * 32 + 16 * (i / DB)) * D;
+        const int db = i % DB;
+        opgt[u] = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]), lds_read_tr16(g_s + rbase + troff[1][db]));
+        opqt[u] = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]), lds_read_tr16(q_s + rbase + troff[1][db]));
+      };
+      tread(0, 0);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 gb = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]),
-                                       lds_read_tr16(g_s + rbase + troff[1][db]));
-          const bf16x8 qbv = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]),
-                                        lds_read_tr16(q_s + rbase + troff[1][db]));
-          dv[db] = mfma_bf16(pa, gb, dv[db]);
-          dk[db] = mfma_bf16(da, qbv, dk[db]);
-        }
+      for (int i = 0; i < NKK; ++i) {
+        if (i + 1 < NKK) tread(i + 1, (i + 1) & 1);
+        dv[i % DB] = mfma_bf16(pa[i / DB], opgt[i & 1], dv[i % DB]);
+        dk[i % DB] = mfma_bf16(da[i / DB], opqt[i & 1], dk[i % DB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -520,15 +539,25 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
         __builtin_amdgcn_sched_barrier(0);
         if (CAUSAL && kt0 + kb * 32 > q_wave0 + 31) continue;  // block wholly above the diagonal
         // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query column).
+        // K and V operands read two k-steps ahead of their MFMAs.
         f32x16 s = f32x16{}, dp = f32x16{};
+        bf16x8 opk[3], opv[3];
+        auto sread = [&](int ks, int u) __attribute__((always_inline)) {
+          opk[u] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
+          opv[u] = as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks]));
+        };
+        sread(0, 0);
+        sread(1, 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s);
-          dp = mfma_bf16(as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks])), gf[ks], dp);
+          if (ks + 2 < KS) sread(ks + 2, (ks + 2) % 3);
+          s = mfma_bf16(opk[ks % 3], qf[ks], s);
+          dp = mfma_bf16(opv[ks % 3], gf[ks], dp);
           if (kb == 0 && fetch) {  // block 0 is never skipped when the wave is live
 #pragma unroll
             for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + 2, n);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
         float cc = c;
         if (need_mask) {
@@ -551,17 +580,27 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
           const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lse2));
           dp[r] = p * (dp[r] - dd);
         }
-        // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read.
+        // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read,
+        // three MFMAs ahead.
+        bf16x8 dsb[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 dsb = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
-                                         dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-          const uint16_t* kt = sk + (kb * 32 + 16 * t) * D;
+        for (int t = 0; t < 2; ++t)
+          dsb[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                               dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
+        constexpr int NKK = 2 * DB;
+        constexpr int PF = 3;
+        auto tread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+          const uint16_t* kt = sk + (kb * 32 + 16 * (i / DB)) * D;
+          return join_u32x2(lds_read_tr16(kt + troff[0][i % DB]), lds_read_tr16(kt + troff[1][i % DB]));
+        };
+        bf16x8 ka[NKK];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 ka = join_u32x2(lds_read_tr16(kt + troff[0][db]), lds_read_tr16(kt + troff[1][db]));
-            dq[db] = mfma_bf16(ka, dsb, dq[db]);
-          }
+        for (int i = 0; i < PF; ++i) ka[i] = tread(i);
+#pragma unroll
+        for (int i = 0; i < NKK; ++i) {
+          if (i + PF < NKK) ka[i + PF] = tread(i + PF);
+          dq[i % DB] = mfma_bf16(ka[i], dsb[i / DB], dq[i % DB]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);

@@ -310,8 +310,8 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
   }
 }
 
-// Staggered form with direct loads.  Eight waves of 32 query rows, two per
-// SIMD, one barrier per interval.  Every wave runs, for each key tile j,
+// Staggered form with direct loads (the default).  Eight waves of 32 query
+// rows, two per SIMD, one barrier per interval.  Every wave runs, for each key tile j,
 //   S_j^T = K_j Q^T (MFMA),  softmax of S_j (VALU),  O^T += V_j^T P_j^T (MFMA),
 // and interval j ends after S_j for late waves and after softmax_j for early
 // waves.  So within an interval an early wave issues P_{j-1} V_{j-1}, S_j and
@@ -323,7 +323,9 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
 // t each wave waits only for its own loads of K_{t+1} and V_t.  Key-validity
 // flags of tile t are read as late as interval t+1 and written two intervals
 // ahead, so they are kept four deep.  ROLE picks the late waves: 0 = waves
-// 4-7, 1 = odd waves.
+// 4-7 (the partner of wave w on its SIMD is w + 4), 1 = odd waves.  The loop
+// is unrolled by the three buffers so that every LDS address is a register
+// plus an immediate.
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE>
 __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtiles) {
   constexpr int NW = 8;
@@ -398,7 +400,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     src_row[i] = row;
     src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
-  auto issue = [&](const uint16_t* src, uint16_t* dst, int j) {
+  auto issue = [&](const uint16_t* src, uint16_t* dst, int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int key = min(j * BC + src_row[i], kv_len - 1);
@@ -406,7 +408,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     }
   };
   uint32_t rvalid = 1u;
-  auto load_flags = [&](int j) {
+  auto load_flags = [&](int j) __attribute__((always_inline)) {
     if constexpr (KPAD) {
       if (wave == 0) {
         const int key = j * BC + lane;
@@ -414,7 +416,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
       }
     }
   };
-  auto store_flags = [&](int j) {
+  auto store_flags = [&](int j) __attribute__((always_inline)) {
     if constexpr (KPAD) {
       if (wave == 0) {
         s_valid[j & 3][lane] = (uint8_t)rvalid;
@@ -438,32 +440,50 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   f32x16 s[2];   // scores of the tile formed last
   bf16x8 p[4];   // packed P of the tile softmaxed last
 
-  auto mma_s = [&](int j) {
-    const uint16_t* kt = sK[j % 3];
+  // The buffer slot (j % 3) is passed as a compile-time constant so that
+  // every LDS address is a register plus an immediate.
+  // The MFMA phases read their LDS operands ahead of use (K two k-steps,
+  // V three MFMAs), so that a wave whose partner is busy with vector work
+  // does not wait a full LDS latency before every MFMA.
+  auto mma_s = [&](auto slot_c) __attribute__((always_inline)) {
+    const uint16_t* kt = sK[decltype(slot_c)::value];
     s[0] = f32x16{};
     s[1] = f32x16{};
+    bf16x8 ka[3][2];
+    auto kread = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int kb = 0; kb < 2; ++kb) dst[kb] = as_bf16x8(*(const u32x4*)(kt + kb * 32 * D + koff[ks]));
+    };
+    kread(0, ka[0]);
+    kread(1, ka[1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma_bf16(as_bf16x8(*(const u32x4*)(kt + kb * 32 * D + koff[ks])), qf[ks], s[kb]);
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(ka[ks % 3][kb], qf[ks], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  auto mma_pv = [&](int j) {
-    const uint16_t* vt = sV[j % 3];
+  auto mma_pv = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int NPV = 4 * DB;
+    constexpr int PF = 3;
+    const uint16_t* vt = sV[decltype(slot_c)::value];
+    auto vread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      const uint16_t* v0 = vt + (i / DB) * 16 * D;  // keys 16 (i / DB) .. +15
+      return join_u32x2(lds_read_tr16(v0 + voff[0][i % DB]), lds_read_tr16(v0 + voff[1][i % DB]));
+    };
+    bf16x8 va[NPV];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < PF; ++i) va[i] = vread(i);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint16_t* v0 = vt + (kb * 32 + 16 * t) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 va = join_u32x2(lds_read_tr16(v0 + voff[0][db]), lds_read_tr16(v0 + voff[1][db]));
-          o[db] = mfma_bf16(va, p[kb * 2 + t], o[db]);
-        }
-      }
+    for (int i = 0; i < NPV; ++i) {
+      if (i + PF < NPV) va[i + PF] = vread(i + PF);
+      o[i % DB] = mfma_bf16(va[i], p[i / DB], o[i % DB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // The VALU block for tile j.
-  auto softmax = [&](int j) {
+  auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kt0 = j * BC;
     bool need_mask = kt0 + BC > kv_len;
     if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
@@ -520,7 +540,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
 
   // Start of interval t: fetch K_{t+2} and V_{t+1} (and the flags of tile
   // t+2, stored at the end of the interval).
-  auto begin_interval = [&](int t) {
+  auto begin_interval = [&](int t) __attribute__((always_inline)) {
     if (t + 2 < ntiles) {
       load_flags(t + 2);
       issue(kp, sK[(t + 2) % 3], t + 2);
@@ -529,7 +549,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   };
   // End of interval t: K_{t+1} and V_t must have landed (the loads of the
   // interval itself may still be in flight), barrier, then start t+1.
-  auto end_interval = [&](int t) {
+  auto end_interval = [&](int t) __attribute__((always_inline)) {
     if (t + 2 < ntiles) store_flags(t + 2);
     const int pending = (t + 2 < ntiles ? LPT : 0) + (t + 1 < ntiles ? LPT : 0);
     if (pending == 2 * LPT) barrier_vmem_n<2 * LPT>();
@@ -554,12 +574,17 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
 
   // Every wave passes ntiles + 1 barriers after the prologue: one per key
   // tile it works on, then the remaining intervals up to ntiles.
-  for (int j = 0; j <= jw_last; ++j) {
-    mma_s(j);
+  auto body = [&](int j, auto slot_c) __attribute__((always_inline)) {
+    mma_s(slot_c);
     if (late) end_interval(j);
     softmax(j);
     if (!late) end_interval(j);
-    mma_pv(j);
+    mma_pv(slot_c);
+  };
+  for (int j = 0; j <= jw_last; j += 3) {
+    body(j, std::integral_constant<int, 0>{});
+    if (j + 1 <= jw_last) body(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 <= jw_last) body(j + 2, std::integral_constant<int, 2>{});
   }
   for (int t = jw_last + 1; t <= ntiles; ++t) end_interval(t);
 
@@ -584,7 +609,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   }
 }
 
-// Direct-load form (the default).  Same per-wave work as fwd_bf16_kernel
+// Direct-load form.  Same per-wave work as fwd_bf16_kernel
 // with one 32-row block per wave, but K and V tiles travel from global memory
 // straight into LDS (global_load_lds_dwordx4: no register staging and no LDS
 // stores) NBUF - 1 tiles ahead, through NBUF buffers per tensor.  Before the
@@ -608,8 +633,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, in
   constexpr int LPT = BC * CPR / NT;     // direct loads per thread per tensor and tile
   constexpr int AHEAD = NBUF - 1;        // tiles in flight ahead of the one in use
   static_assert(LPT * NT == BC * CPR, "tile chunks must divide evenly");
-  static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
-  static_assert(AHEAD * 2 * LPT < 16, "vmcnt field of 4 bits");
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four buffers");
+  static_assert(AHEAD * 2 * LPT < 64, "vmcnt field of 6 bits");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
@@ -723,18 +748,27 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, in
     // an idle wave issues them at once.
     if (fetch && !wave_live) issue(j + AHEAD);
     if (wave_live) {
+      // K operands are read two k-steps ahead of their MFMAs.
       f32x16 s[2];
       s[0] = f32x16{};
       s[1] = f32x16{};
+      bf16x8 ka[3][2];
+      auto kread = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dst[kb] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
+      };
+      kread(0, ka[0]);
+      kread(1, ka[1]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          s[kb] = mfma_bf16(as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks])), qf[ks], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(ka[ks % 3][kb], qf[ks], s[kb]);
         if (fetch) {
 #pragma unroll
           for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + AHEAD, n);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       bool need_mask = kt0 + BC > kv_len;
@@ -789,22 +823,33 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, in
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= a_;
       }
+      // O^T += V^T P^T; V operands are read three MFMAs ahead.
+      {
+        constexpr int NPV = 4 * DB;
+        constexpr int PF = 3;
+        auto vread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+          const uint16_t* v0 = svt + (i / DB) * 16 * D;  // keys 16 (i / DB) .. +15
+          return join_u32x2(lds_read_tr16(v0 + voff[0][i % DB]), lds_read_tr16(v0 + voff[1][i % DB]));
+        };
+        bf16x8 va[NPV];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < PF; ++i) va[i] = vread(i);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint16_t* v0 = svt + (kb * 32 + 16 * t) * D;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 va = join_u32x2(lds_read_tr16(v0 + voff[0][db]), lds_read_tr16(v0 + voff[1][db]));
-            o[db] = mfma_bf16(va, pb[kb * 2 + t], o[db]);
-          }
+        for (int i = 0; i < NPV; ++i) {
+          if (i + PF < NPV) va[i + PF] = vread(i + PF);
+          o[i % DB] = mfma_bf16(va[i], pb[i / DB], o[i % DB]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
     if (fetch) store_flags(NU);
     // this wave's loads of tile j + 1 have landed (those issued after them,
     // for tiles j + 2 .. j + AHEAD, may not have)
-    if constexpr (AHEAD == 2) {
+    if constexpr (AHEAD == 3) {
+      if (fetch) barrier_vmem_n<4 * LPT>();
+      else if (j + 2 < ntiles) barrier_vmem_n<2 * LPT>();
+      else barrier_vmem_n<0>();
+    } else if constexpr (AHEAD == 2) {
       if (fetch) barrier_vmem_n<2 * LPT>();
       else barrier_vmem_n<0>();
     } else {
@@ -836,8 +881,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, in
   for (int j = 0; j < ntiles; j += NBUF) {
     step(j, std::integral_constant<int, 0>{});
     if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
-    if constexpr (NBUF == 3) {
+    if constexpr (NBUF >= 3) {
       if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
+    }
+    if constexpr (NBUF >= 4) {
+      if (j + 3 < ntiles) step(j + 3, std::integral_constant<int, 3>{});
     }
   }
 
@@ -935,9 +983,14 @@ static hipError_t dispatch_fwd(const AttnArgs& a, bool causal, bool varlen, bool
 }
 
 // Kernel variants.  MIATTN_FWD_TILE=<n> picks one for tuning sweeps:
-//   0 (default) the direct-load form;
-//   1, 2 the staggered form with either choice of late waves;
-//   3 one 32-row block per wave with register-staged tiles.
+//   0 (default) the staggered form, late waves 4-7;
+//   1 the direct-load form (eight waves, three buffers);
+//   2 the staggered form with odd late waves;
+//   3 one 32-row block per wave with register-staged tiles;
+//   4 the four-wave form with 64 rows per wave (fwd_w4.hip);
+//   5 the direct-load form with four waves and two buffers (two
+//     workgroups per CU);
+//   6 the direct-load form with four buffers (loads three tiles ahead).
 static int fwd_tile_choice() {
   static int choice = [] {
     const char* e = getenv("MIATTN_FWD_TILE");
@@ -949,19 +1002,22 @@ static int fwd_tile_choice() {
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream) {
   const bool kpad = varlen && a.key_valid != nullptr;
   const int t = fwd_tile_choice();
+  if (t == 4) return launch_fwd_w4_bf16(a, d, causal, varlen, stream);
   if (d == 128) {
-    if (t == 1) return dispatch_fwd_stag<128, 0>(a, causal, varlen, kpad, stream);
+    if (t == 1) return dispatch_fwd_dma<128, 8, 3>(a, causal, varlen, kpad, stream);
     if (t == 2) return dispatch_fwd_stag<128, 1>(a, causal, varlen, kpad, stream);
     if (t == 3) return dispatch_fwd<128, 1, 8, 1>(a, causal, varlen, kpad, stream);
     if (t == 5) return dispatch_fwd_dma<128, 4, 2>(a, causal, varlen, kpad, stream);
-    return dispatch_fwd_dma<128, 8, 3>(a, causal, varlen, kpad, stream);
+    if (t == 6) return dispatch_fwd_dma<128, 8, 4>(a, causal, varlen, kpad, stream);
+    return dispatch_fwd_stag<128, 0>(a, causal, varlen, kpad, stream);
   }
   if (d == 64) {
-    if (t == 1) return dispatch_fwd_stag<64, 0>(a, causal, varlen, kpad, stream);
+    if (t == 1) return dispatch_fwd_dma<64, 8, 3>(a, causal, varlen, kpad, stream);
     if (t == 2) return dispatch_fwd_stag<64, 1>(a, causal, varlen, kpad, stream);
     if (t == 3) return dispatch_fwd<64, 1, 8, 1>(a, causal, varlen, kpad, stream);
     if (t == 5) return dispatch_fwd_dma<64, 4, 2>(a, causal, varlen, kpad, stream);
-    return dispatch_fwd_dma<64, 8, 3>(a, causal, varlen, kpad, stream);
+    if (t == 6) return dispatch_fwd_dma<64, 8, 4>(a, causal, varlen, kpad, stream);
+    return dispatch_fwd_stag<64, 0>(a, causal, varlen, kpad, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -234,7 +234,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
 // from moving memory accesses across it.
 template <int N>
 __device__ __forceinline__ void barrier_vmem_n() {
-  static_assert(N >= 0 && N < 16, "vmcnt field of 4 bits used here");
+  static_assert(N >= 0 && N < 64, "vmcnt field of 6 bits");
   __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
