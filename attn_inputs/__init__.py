@@ -57,14 +57,17 @@ def _draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarr
 
 
 def dense_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
-                 sigma_qk: float = 1.0, sigma_vdo: float = 1.0, with_do: bool = True) -> dict:
-    """Q, K, V (and dO) of shape [B, H, N, d] as float32 holding dtype-exact values."""
+                 sigma_qk: float = 1.0, sigma_vdo: float = 1.0, with_do: bool = True,
+                 kv_heads: int | None = None) -> dict:
+    """Q, K, V (and dO) of shape [B, H, N, d] as float32 holding dtype-exact values.
+    With ``kv_heads`` K and V have that many heads instead: [B, kv_heads, N, d]."""
     rng = np.random.default_rng(seed)
     shape = (B, H, N, d)
+    kv_shape = (B, H if kv_heads is None else kv_heads, N, d)
     out = {
         "q": _draw(rng, shape, sigma_qk, dtype),
-        "k": _draw(rng, shape, sigma_qk, dtype),
-        "v": _draw(rng, shape, sigma_vdo, dtype),
+        "k": _draw(rng, kv_shape, sigma_qk, dtype),
+        "v": _draw(rng, kv_shape, sigma_vdo, dtype),
     }
     if with_do:
         out["do"] = _draw(rng, shape, sigma_vdo, dtype)

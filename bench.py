@@ -8,7 +8,9 @@ Inputs are seeded synthetic tensors already resident in HBM before the timed
 region.
 
 Workload (default): causal self-attention, B=4, H=32, N=4096, d=128, bf16,
-scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) rounded to bf16, seed 0.
+scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) rounded to bf16, seed 0.  With grouped
+key/value heads (H_kv < H) the step is attn_fwd_gqa + attn_bwd_gqa and the
+backward is timed as one call (its three kernels are not split by events).
 
 FLOP accounting: forward 4*B*H*N^2*d, halved under the causal mask; backward
 2.5x the forward (five N^2*d products, the recompute of S included).  The
@@ -42,6 +44,8 @@ WORKLOADS = {
     "causal_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128, causal=True, sigma_qk=1.0),
     "causal_b1_h16_n16384_d128": dict(B=1, H=16, N=16384, d=128, causal=True, sigma_qk=1.5),
     "noncausal_b8_h16_n2048_d64": dict(B=8, H=16, N=2048, d=64, causal=False, sigma_qk=1.0),
+    # grouped key/value heads: 32 query heads share 8 K/V heads (groups of 4)
+    "gqa_causal_b4_h32_hkv8_n4096_d128": dict(B=4, H=32, Hkv=8, N=4096, d=128, causal=True, sigma_qk=1.0),
 }
 DEFAULT = "causal_b4_h32_n4096_d128"
 METRIC = "attn fwd/bwd TFLOPS + % MFMA bf16 peak, causal B4 H32 N4096 d128, 1 MI355X"
@@ -91,11 +95,13 @@ def cpu_baseline(inp, cfg, scale, budget_s=10.0):
     from oracle import attention as A
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    G = H // cfg.get("Hkv", H)
     heads = 0
     t0 = time.perf_counter()
     while heads < B * H:
         b, h = divmod(heads, H)
-        A.head_backward(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], inp["do"][b, h], scale, cfg["causal"])
+        A.head_backward(inp["q"][b, h], inp["k"][b, h // G], inp["v"][b, h // G], inp["do"][b, h], scale,
+                        cfg["causal"])
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -153,18 +159,32 @@ def main(argv=None):
 
     cfg = WORKLOADS[args.workload]
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
+    Hkv = cfg.get("Hkv", H)
+    grouped = Hkv != H
     scale = 1.0 / math.sqrt(d)
     log(f"workload {args.workload}: generating inputs")
-    inp = dense_inputs(B, H, N, d, "bf16", seed=0, sigma_qk=cfg["sigma_qk"])
+    inp = dense_inputs(B, H, N, d, "bf16", seed=0, sigma_qk=cfg["sigma_qk"], kv_heads=Hkv if grouped else None)
     dev = {n: torch.from_numpy(inp[n]).to(torch.bfloat16).cuda().contiguous() for n in ("q", "k", "v", "do")}
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(M.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
+    def step_grouped(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.attn_fwd_gqa(q, k, v, o, lse, scale, causal, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.attn_bwd_gqa(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
     def step(ev=None):
+        if grouped:
+            return step_grouped(ev)
         if ev is not None:
             ev[0].record(stream)
         M.attn_fwd(q, k, v, o, lse, scale, causal, stream)
@@ -194,38 +214,55 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per = {"fwd": [], "bwd_prep": [], "bwd_dkdv": [], "bwd_dq": [], "step": []}
+    per = {"fwd": [], "bwd_prep": [], "bwd_dkdv": [], "bwd_dq": [], "bwd": [], "step": []}
     for ev in events:
         per["fwd"].append(ev[0].elapsed_time(ev[1]))
-        per["bwd_prep"].append(ev[1].elapsed_time(ev[2]))
-        per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
-        per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
+        per["bwd"].append(ev[1].elapsed_time(ev[4]))
         per["step"].append(ev[0].elapsed_time(ev[4]))
+        if not grouped:
+            per["bwd_prep"].append(ev[1].elapsed_time(ev[2]))
+            per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
+            per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
+    per = {k_: v_ for k_, v_ in per.items() if v_}
     mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
     med = {k_: statistics.median(v_) for k_, v_ in per.items()}
 
     f_fwd, f_bwd = flops(B, H, N, d, causal)
     ms_step = wall * 1e3 / args.steps
-    bwd_ms = mean["bwd_prep"] + mean["bwd_dkdv"] + mean["bwd_dq"]
+    bwd_ms = mean["bwd"]
     f_dkdv, f_dq = 2.0 * f_fwd, 1.5 * f_fwd
     tflops_fwd = f_fwd / (mean["fwd"] * 1e-3) / 1e12
     tflops_bwd = f_bwd / (bwd_ms * 1e-3) / 1e12
-    tflops_dkdv = f_dkdv / (mean["bwd_dkdv"] * 1e-3) / 1e12
-    tflops_dq = f_dq / (mean["bwd_dq"] * 1e-3) / 1e12
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
-    elem = B * H * N * d
+    elem_q = B * H * N * d
+    elem_kv = B * Hkv * N * d
     rows = B * H * N
-    prep_bytes = 2 * elem * 2 + rows * 4                  # read O, dO; write D
-    fwd_bytes = 3 * elem * 2 + elem * 2 + rows * 4         # read Q, K, V; write O, LSE
-    # dominant kernel for the roofline: the longest of the three MFMA kernels
-    kern = {"fwd_stag_kernel (attn_fwd)": (mean["fwd"], f_fwd),
-            "bwd_dkdv_kernel (attn_bwd_dkdv)": (mean["bwd_dkdv"], f_dkdv),
-            "bwd_dq_kernel (attn_bwd_dq)": (mean["bwd_dq"], f_dq)}
+    prep_bytes = 2 * elem_q * 2 + rows * 4                          # read O, dO; write D
+    fwd_bytes = 2 * elem_q * 2 + 2 * elem_kv * 2 + rows * 4         # read Q, K, V; write O, LSE
+    bwd = {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
+           "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2)}
+    # dominant kernel for the roofline: the longest of the MFMA kernels whose
+    # launches the events bracket one by one
+    kern = {"fwd_stag_kernel (attn_fwd)": (mean["fwd"], f_fwd)}
+    if not grouped:
+        tflops_dkdv = f_dkdv / (mean["bwd_dkdv"] * 1e-3) / 1e12
+        tflops_dq = f_dq / (mean["bwd_dq"] * 1e-3) / 1e12
+        bwd.update({"prep_ms": round(mean["bwd_prep"], 4),
+                    "prep_gbps": round(prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9, 1),
+                    "prep_pct_hbm_peak": round(100 * prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                               2),
+                    "dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
+                    "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2)})
+        kern["bwd_dkdv_kernel (attn_bwd_dkdv)"] = (mean["bwd_dkdv"], f_dkdv)
+        kern["bwd_dq_kernel (attn_bwd_dq)"] = (mean["bwd_dq"], f_dq)
+    else:
+        kern = {"fwd_stag_kernel (attn_fwd_gqa)": (mean["fwd"], f_fwd)}
     dom = max(kern, key=lambda k_: kern[k_][0])
     dom_ms, dom_flops = kern[dom]
     dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
 
+    heads = f"H{H}" + (f" H_kv{Hkv}" if grouped else "")
     result = {
         "metric": METRIC if args.workload == DEFAULT else f"attn fwd+bwd TFLOPS, {args.workload}, 1 MI355X",
         "value": round(value, 3),
@@ -240,18 +277,12 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"exact attention fwd+bwd, {'causal' if causal else 'non-causal'} "
-                               f"B{B} H{H} N{N} d{d} bf16", "B": B, "H": H, "N": N, "d": d,
+                               f"B{B} {heads} N{N} d{d} bf16", "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d,
                    "causal": causal, "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd},
         "fwd": {"ms": round(mean["fwd"], 4), "ms_median": round(med["fwd"], 4), "tflops": round(tflops_fwd, 2),
                 "pct_mfma_peak": round(100 * tflops_fwd / PEAK_BF16_TFLOPS, 2),
                 "gbps": round(fwd_bytes / (mean["fwd"] * 1e-3) / 1e9, 1)},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
-                "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2),
-                "prep_ms": round(mean["bwd_prep"], 4),
-                "prep_gbps": round(prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9, 1),
-                "prep_pct_hbm_peak": round(100 * prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-                "dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
-                "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2)},
+        "bwd": bwd,
         "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),

@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_bwd_preprocess": (_I, [_P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "attn_bwd_dkdv": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_bwd_dq": (_I, [_P] * 6 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_gqa": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_f32": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_varlen": (_I, [_P] * 5 + [_P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
@@ -144,6 +146,27 @@ def attn_bwd_dq(q, k, v, lse, dO, dq, scale: float, causal: bool, workspace, str
     _check("attn_bwd_dq", load().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(dq), B, H, N, d,
                                              float(scale), int(bool(causal)), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def _gqa_dims(q, k):
+    B, H, N, d = _dense_dims(q)
+    if k.dim() != 4 or int(k.shape[0]) != B or int(k.shape[2]) != N or int(k.shape[3]) != d:
+        raise ValueError("grouped K/V are [B, H_kv, N, d] with the B, N, d of Q")
+    return B, H, int(k.shape[1]), N, d
+
+
+def attn_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    B, H, Hkv, N, d = _gqa_dims(q, k)
+    _check("attn_fwd_gqa", load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                               float(scale), int(bool(causal)), _stream(stream)))
+
+
+def attn_bwd_gqa(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    B, H, Hkv, N, d = _gqa_dims(q, k)
+    _check("attn_bwd_gqa", load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
+                                               int(bool(causal)), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def attn_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

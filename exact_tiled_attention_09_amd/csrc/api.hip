@@ -63,6 +63,7 @@ AttnArgs dense_args(const void* q, const void* k, const void* v, const void* o, 
   a.lse = const_cast<float*>(lse);
   a.B = B;
   a.H = H;
+  a.Hkv = H;
   a.N = N;
   a.total_tokens = 0;
   a.scale = scale;
@@ -158,6 +159,38 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const int64_t rows = (int64_t)B * H * N;
   if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
   AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, workspace, rows);
+  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
+  if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                 int d, float scale, int causal, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  if (H_kv <= 0 || H <= 0 || H % H_kv != 0) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.Hkv = H_kv;
+  return hip_status(miattn::launch_fwd_bf16(a, d, causal != 0, false, stream));
+}
+
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                 void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (H_kv <= 0 || H <= 0 || H % H_kv != 0) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.Hkv = H_kv;
   a.dout = dO;
   a.dq = dq;
   a.dk = dk;

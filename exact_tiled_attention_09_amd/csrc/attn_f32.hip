@@ -35,8 +35,8 @@ __global__ void __launch_bounds__(64, 1) fwd_f32_kernel(AttnArgs a, int n_qtiles
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hi = lane >> 5;
   const float* __restrict__ qp = (const float*)a.q + sv.base;
-  const float* __restrict__ kp = (const float*)a.k + sv.base;
-  const float* __restrict__ vp = (const float*)a.v + sv.base;
+  const float* __restrict__ kp = (const float*)a.k + sv.kv_base;
+  const float* __restrict__ vp = (const float*)a.v + sv.kv_base;
   float c = a.scale_log2;
   const float qsign = c < 0.f ? -1.f : 1.f;
   c = fabsf(c);
@@ -167,8 +167,8 @@ __global__ void __launch_bounds__(64, 1) bwd_main_f32_kernel(AttnArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const float c = a.scale_log2;
   const float* __restrict__ qp = (const float*)a.q + sv.base;
-  const float* __restrict__ kp = (const float*)a.k + sv.base;
-  const float* __restrict__ vp = (const float*)a.v + sv.base;
+  const float* __restrict__ kp = (const float*)a.k + sv.kv_base;
+  const float* __restrict__ vp = (const float*)a.v + sv.kv_base;
   const float* __restrict__ gp = (const float*)a.dout + sv.base;
 
   const int my_key = k0 + l32;

@@ -102,11 +102,18 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // LSE * log2(e), +inf if dead
   __shared__ __attribute__((aligned(16))) float sDv[2][BQ];  // D
 
+  // One workgroup per (sequence, key/value head, key tile).  With grouped
+  // heads it runs the query-tile loop once for each of the G query heads
+  // that read this key/value head, so dK and dV sum over the group in
+  // registers.
   int bh, kt;
-  wg_coords(blockIdx.x, a.B * a.H, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const SeqView sv = seq_view<VARLEN>(a, b, h, D);
+  wg_coords(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
+  const int G = a.H / a.Hkv;
+  const int b = bh / a.Hkv;
+  const int hk = bh - b * a.Hkv;
+  const SeqView sv = seq_view<VARLEN>(a, b, hk * G, D);  // query head hk*G: the first of the group
+  const int64_t qhs = q_head_stride<VARLEN>(a, D);
+  const int64_t rhs = row_head_stride<VARLEN>(a);
   const int k0 = kt * BK;
   if (k0 >= sv.len) return;
 
@@ -121,8 +128,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   const int qh0 = NW == 4 ? 0 : (wave >> 2); // first query half handled
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
   const uint16_t* __restrict__ gp = (const uint16_t*)a.dout + sv.base;
 
   const int wk0 = k0 + kblk * 32;  // this wave's 32 keys
@@ -142,6 +149,24 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
 
   const int n_qt = (len + BQ - 1) / BQ;
   const int qt_begin = CAUSAL ? k0 / BQ : 0;
+  // Steps v = 0 .. nv-1 run query tile qt_begin + v % nsteps of the group's
+  // query head v / nsteps.  The tile and head of the step to fetch next are
+  // kept incrementally (tile nit of the head whose Q / dO start at nq / ng and
+  // whose LSE / D rows start at nrow), so the loop does no division.
+  const int nsteps = n_qt - qt_begin;
+  const int nv = G * nsteps;
+  int nit = qt_begin;
+  const uint16_t* nq = qp;
+  const uint16_t* ng = gp;
+  int64_t nrow = sv.row_base;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++nit == n_qt) {
+      nit = qt_begin;
+      nq += qhs;
+      ng += qhs;
+      nrow += rhs;
+    }
+  };
 
   // Q and dO tiles travel from global memory straight into LDS (direct
   // loads; LDS chunk p = i*NT + tid of a tile holds row p / CH_PER_ROW, logical
@@ -155,17 +180,17 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     src_row[i] = row;
     src_col[i] = ((pch % CH_PER_ROW) ^ swz<D>(row)) << 3;
   }
-  // Load number n (0 .. 2*QCPT-1) of this thread for tile it: Q for even n,
-  // dO for odd n, chunk n / 2.
-  auto issue_part = [&](int it, int buf, int n) {
+  // Load number n (0 .. 2*QCPT-1) of this thread for the step to fetch
+  // next: Q for even n, dO for odd n, chunk n / 2.
+  auto issue_part = [&](int buf, int n) {
     const int i = n >> 1;
-    const int64_t off = (int64_t)min(it * BQ + src_row[i], len - 1) * sv.tok_stride + src_col[i];
-    if (n & 1) lds_dma16(gp + off, sGb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
-    else lds_dma16(qp + off, sQb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
+    const int64_t off = (int64_t)min(nit * BQ + src_row[i], len - 1) * sv.tok_stride + src_col[i];
+    if (n & 1) lds_dma16(ng + off, sGb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
+    else lds_dma16(nq + off, sQb + buf * QT_ELEMS + (i * NT + wave * 64) * 8);
   };
-  auto issue_tile = [&](int it, int buf) {
+  auto issue_tile = [&](int buf) {
 #pragma unroll
-    for (int n = 0; n < 2 * QCPT; ++n) issue_part(it, buf, n);
+    for (int n = 0; n < 2 * QCPT; ++n) issue_part(buf, n);
   };
   // LSE (as log2, +inf when the row is dead or past the end) and D of the
   // tile's rows, through registers of wave 0 (BQ = 64 rows, one per lane).
@@ -174,12 +199,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   static_assert(BQ == 64, "one row per lane of wave 0");
   float rl = 0.f, rd = 0.f;
   int rq = 0;
-  auto load_rows = [&](int it) {
+  auto load_rows = [&]() {
     if (wave == 0) {
-      rq = it * BQ + lane;
-      const int qc = min(rq, len - 1);
-      rl = a.lse[sv.row_base + qc];
-      rd = a.dvec[sv.row_base + qc];
+      rq = nit * BQ + lane;
+      const int64_t row = nrow + min(rq, len - 1);
+      rl = a.lse[row];
+      rd = a.dvec[row];
     }
   };
   auto store_rows = [&](int buf) {
@@ -192,7 +217,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
 
   // Prologue: the first Q/dO tile in flight, then K and V (rows past the
   // sequence are zero) and the first LSE/D rows; one wait covers all.
-  if (qt_begin < n_qt) issue_tile(qt_begin, 0);
+  issue_tile(0);
 #pragma unroll
   for (int cidx = 0; cidx < KCPT; ++cidx) {
     const int chunk = tid + cidx * NT;
@@ -201,16 +226,14 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     const int key = k0 + row;
     const int kc = min(key, len - 1);
     const uint32_t keep = key < len ? 0xffffffffu : 0u;
-    const u32x4 xk = *(const u32x4*)(kp + (int64_t)kc * sv.tok_stride + col) & keep;
-    const u32x4 xv = *(const u32x4*)(vp + (int64_t)kc * sv.tok_stride + col) & keep;
+    const u32x4 xk = *(const u32x4*)(kp + (int64_t)kc * sv.kv_stride + col) & keep;
+    const u32x4 xv = *(const u32x4*)(vp + (int64_t)kc * sv.kv_stride + col) & keep;
     const int off = swz_off<D>(row, col);
     *(u32x4*)(sK + off) = xk;
     *(u32x4*)(sV + off) = xv;
   }
-  if (qt_begin < n_qt) {
-    load_rows(qt_begin);
-    store_rows(0);
-  }
+  load_rows();
+  store_rows(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first Q/dO tile too
   barrier_vmem_n<0>();
 
@@ -228,13 +251,15 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   const uint16_t* kb_rows = sK + kblk * 32 * D;
   const uint16_t* vb_rows = sV + kblk * 32 * D;
 
-  // One query tile from buffer BUF (= (it - qt_begin) % 2, a compile-time
-  // constant so that every LDS address is a register plus an immediate).
-  auto step = [&](int it, auto buf_c) {
+  // Step v from buffer BUF (= v % 2, a compile-time constant so that every
+  // LDS address is a register plus an immediate).
+  auto step = [&](int v, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
+    const int it = nit;
+    advance();
     const int q0 = it * BQ;
-    const bool fetch = it + 1 < n_qt;
-    if (fetch) load_rows(it + 1);
+    const bool fetch = v + 1 < nv;
+    if (fetch) load_rows();
     // The loads of tile it+1 are spread over the first live half's S / dP
     // MFMAs (all waves issuing together would queue in the CU's memory
     // pipeline); a wave with no live half issues them at once.
@@ -267,7 +292,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
         dp = mfma_bf16(opg[ks & 1], opv[ks & 1], dp);
         if (pending) {
 #pragma unroll
-          for (int n = ks * 2 * QCPT / KS; n < (ks + 1) * 2 * QCPT / KS; ++n) issue_part(it + 1, buf ^ 1, n);
+          for (int n = ks * 2 * QCPT / KS; n < (ks + 1) * 2 * QCPT / KS; ++n) issue_part(buf ^ 1, n);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -328,13 +353,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    if (pending) issue_tile(it + 1, buf ^ 1);
+    if (pending) issue_tile(buf ^ 1);
     if (fetch) store_rows(buf ^ 1);
     barrier_vmem_n<0>();  // the next tile has landed
   };
-  for (int it = qt_begin; it < n_qt; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
+  for (int v = 0; v < nv; v += 2) {
+    step(v, std::integral_constant<int, 0>{});
+    if (v + 1 < nv) step(v + 1, std::integral_constant<int, 1>{});
   }
 
   if constexpr (NW == 8) {
@@ -361,15 +386,15 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   }
 
   // dK = scale * acc, dV = acc; accumulator rows are keys, columns features.
-  uint16_t* __restrict__ dkp = (uint16_t*)a.dk + sv.base;
-  uint16_t* __restrict__ dvp = (uint16_t*)a.dv + sv.base;
+  uint16_t* __restrict__ dkp = (uint16_t*)a.dk + sv.kv_base;
+  uint16_t* __restrict__ dvp = (uint16_t*)a.dv + sv.kv_base;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = wk0 + (r >> 2) * 8 + hi * 4 + (r & 3);
     if (key < len) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int64_t off = (int64_t)key * sv.tok_stride + db * 32 + l32;
+        const int64_t off = (int64_t)key * sv.kv_stride + db * 32 + l32;
         const uint32_t kb = pack_bf16x2(dk[db][r] * a.scale, 0.f);
         const uint32_t vb = pack_bf16x2(dv[db][r], 0.f);
         dkp[off] = (uint16_t)(kb & 0xffffu);
@@ -420,8 +445,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   const float c = a.scale_log2;
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
   const uint16_t* __restrict__ gp = (const uint16_t*)a.dout + sv.base;
 
   const bool row_ok = qi < sv.len;
@@ -447,7 +472,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   auto issue_part = [&](int j, int n) {
     const int i = n >> 1;
     const int key = min(j * BC + src_row[i], kv_len - 1);
-    const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
+    const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
     if (n & 1) lds_dma16(vp + off, sV[j % 3] + (i * NT + wave * 64) * 8);
     else lds_dma16(kp + off, sK[j % 3] + (i * NT + wave * 64) * 8);
   };
@@ -663,7 +688,7 @@ template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
 static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BK = 128;
   const int n_ktiles = (a.N + BK - 1) / BK;
-  const int64_t blocks = (int64_t)n_ktiles * a.B * a.H;
+  const int64_t blocks = (int64_t)n_ktiles * a.B * a.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (dkdv_waves() == 4)

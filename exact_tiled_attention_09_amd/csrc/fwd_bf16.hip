@@ -72,8 +72,8 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
   const int q_wave0 = q_tile0 + wave * QB * 32;
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
 
   // A negative scale is handled by flipping the sign of Q once.
   float c = a.scale_log2;
@@ -121,8 +121,8 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
       const int key = j * BC + row;
       u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
       if (key < kv_len) {
-        zk = *(const u32x4*)(kp + (int64_t)key * sv.tok_stride + col);
-        zv = *(const u32x4*)(vp + (int64_t)key * sv.tok_stride + col);
+        zk = *(const u32x4*)(kp + (int64_t)key * sv.kv_stride + col);
+        zv = *(const u32x4*)(vp + (int64_t)key * sv.kv_stride + col);
       }
       rk[cidx] = zk;
       rv[cidx] = zv;
@@ -362,8 +362,8 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   const int kv_len = sv.len;
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
 
   float c = a.scale_log2;
   const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
@@ -404,7 +404,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int key = min(j * BC + src_row[i], kv_len - 1);
-      lds_dma16(src + (int64_t)key * sv.tok_stride + src_col[i], dst + (i * NT + wave * 64) * 8);
+      lds_dma16(src + (int64_t)key * sv.kv_stride + src_col[i], dst + (i * NT + wave * 64) * 8);
     }
   };
   uint32_t rvalid = 1u;
@@ -658,8 +658,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, in
   const int kv_len = sv.len;
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
 
   float c = a.scale_log2;
   const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
@@ -689,7 +689,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, in
   auto issue_part = [&](int j, int n) {
     const int i = n >> 1;
     const int key = min(j * BC + src_row[i], kv_len - 1);
-    const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
+    const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
     if (n & 1) lds_dma16(vp + off, sV[j % NBUF] + (i * NT + wave * 64) * 8);
     else lds_dma16(kp + off, sK[j % NBUF] + (i * NT + wave * 64) * 8);
   };

@@ -208,8 +208,8 @@ __global__ void __launch_bounds__(256, 1) fwd_w4_kernel(AttnArgs a, int n_qtiles
   const int kv_len = sv.len;
 
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.base;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
+  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
 
   // A negative scale is handled by flipping the sign of Q once.
   float c = a.scale_log2;
@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(256, 1) fwd_w4_kernel(AttnArgs a, int n_qtiles
   auto issue_part = [&](int j, int n) {
     const int i = n >> 1;
     const int key = min(j * BC + src_row[i], kv_len - 1);
-    const int64_t off = (int64_t)key * sv.tok_stride + src_col[i];
+    const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
     if (n & 1) lds_dma16(vp + off, sV[j % NBUF] + (i * NT + wave * 64) * 8);
     else lds_dma16(kp + off, sK[j % NBUF] + (i * NT + wave * 64) * 8);
   };

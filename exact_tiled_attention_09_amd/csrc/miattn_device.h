@@ -53,17 +53,21 @@ struct AttnArgs {
   const int* cu_seqlens;
   const uint8_t* key_valid;  // per packed token, nonzero = valid key (nullable)
   int B;           // dense: batch; packed: number of sequences
-  int H;
+  int H;           // query heads (Q, O, dO, dQ, LSE, D)
+  int Hkv;         // key/value heads (K, V, dK, dV); divides H, query head h
+                   // reads key/value head h / (H / Hkv); Hkv == H without grouping
   int N;           // dense: sequence length; packed: longest sequence
   int total_tokens;
   float scale;     // multiplies Q K^T
   float scale_log2;  // scale * log2(e)
 };
 
-// Where one (sequence, head) lives.
+// Where one (sequence, query head) lives, and the key/value head it reads.
 struct SeqView {
-  int64_t base;        // element offset of token 0, feature 0
-  int64_t tok_stride;  // elements between consecutive tokens
+  int64_t base;        // Q/O/dO/dQ element offset of token 0, feature 0
+  int64_t tok_stride;  // elements between consecutive tokens of Q/O/dO/dQ
+  int64_t kv_base;     // K/V/dK/dV element offset of token 0, feature 0
+  int64_t kv_stride;   // elements between consecutive tokens of K/V/dK/dV
   int64_t row_base;    // offset of token 0 in LSE / D
   int64_t tok0;        // packed index of token 0 (key_valid indexing)
   int len;
@@ -72,22 +76,38 @@ struct SeqView {
 template <bool VARLEN>
 __device__ __forceinline__ SeqView seq_view(const AttnArgs& a, int b, int h, int D) {
   SeqView s;
+  const int hk = h / (a.H / a.Hkv);
   if constexpr (VARLEN) {
     const int t0 = a.cu_seqlens[b];
     const int t1 = a.cu_seqlens[b + 1];
     s.base = ((int64_t)t0 * a.H + h) * D;
     s.tok_stride = (int64_t)a.H * D;
+    s.kv_base = ((int64_t)t0 * a.Hkv + hk) * D;
+    s.kv_stride = (int64_t)a.Hkv * D;
     s.row_base = (int64_t)h * a.total_tokens + t0;
     s.tok0 = t0;
     s.len = t1 - t0;
   } else {
     s.base = ((int64_t)b * a.H + h) * (int64_t)a.N * D;
     s.tok_stride = D;
+    s.kv_base = ((int64_t)b * a.Hkv + hk) * (int64_t)a.N * D;
+    s.kv_stride = D;
     s.row_base = ((int64_t)b * a.H + h) * (int64_t)a.N;
     s.tok0 = (int64_t)b * a.N;
     s.len = a.N;
   }
   return s;
+}
+
+// Offsets of query head h within a group view: Q/O/dO/dQ element offset and
+// LSE/D offset move by these per head.
+template <bool VARLEN>
+__device__ __forceinline__ int64_t q_head_stride(const AttnArgs& a, int D) {
+  return VARLEN ? (int64_t)D : (int64_t)a.N * D;
+}
+template <bool VARLEN>
+__device__ __forceinline__ int64_t row_head_stride(const AttnArgs& a) {
+  return VARLEN ? (int64_t)a.total_tokens : (int64_t)a.N;
 }
 
 // Workgroup -> (sequence*head, tile), tile-major: every head's tile t before any

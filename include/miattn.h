@@ -125,6 +125,28 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, c
                 int B, int H, int N, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Forward with grouped key/value heads (grouped-query attention; H_kv = 1 is
+ * multi-query attention), dense bf16.  q, o: [B,H,N,d]; k, v: [B,H_kv,N,d];
+ * lse: [B,H,N] fp32.  H_kv must divide H; query head h attends with key/value
+ * head h / (H / H_kv).  Everything else as attn_fwd, which is the case
+ * H_kv == H.  MQA and GQA are described in "第 18 章 FlashAttention" section
+ * 18.2.2 (groups of query heads share one K/V head, loaded once and reused
+ * across the group) and section 18.7.1 (an interface whose K/V carry fewer
+ * heads than Q, broadcast when the query head count is a multiple of it).
+ * MIATTN_ERR_INVALID_ARG also when H_kv <= 0 or H % H_kv != 0. */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int H_kv, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Backward with grouped key/value heads, dense bf16.  q, o, dO, dq:
+ * [B,H,N,d]; k, v, dk, dv: [B,H_kv,N,d]; lse: [B,H,N].  dk and dv of a
+ * key/value head are the sums over the H / H_kv query heads that read it
+ * (taken in fp32 registers by one workgroup, no atomics; bitwise
+ * reproducible).  workspace: attn_bwd_workspace_bytes(B,H,N,d) bytes. */
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dO, void* dq, void* dk, void* dv,
+                 int B, int H, int H_kv, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* fp32 forward: same contract as attn_fwd with fp32 q, k, v, o. */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);

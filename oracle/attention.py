@@ -37,6 +37,8 @@ __all__ = [
     "backward",
     "varlen_forward",
     "varlen_backward",
+    "gqa_forward",
+    "gqa_backward",
 ]
 
 
@@ -248,4 +250,52 @@ def varlen_backward(q, k, v, do, cu_seqlens, scale, causal=False, key_valid=None
         dq, dk, dv, o, lse, dvec = head_backward(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], scale, causal, kv)
         out["dq"][a:b, h], out["dk"][a:b, h], out["dv"][a:b, h], out["o"][a:b, h] = dq, dk, dv, o
         out["lse"][h, a:b], out["D"][h, a:b] = lse, dvec
+    return out
+
+
+def _group(H, Hkv):
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError("the key/value head count must divide the query head count")
+    return H // Hkv
+
+
+def gqa_forward(q, k, v, scale, causal=False, heads=None):
+    """Grouped key/value heads, dense layout: q [B, H, N, d], k and v
+    [B, H_kv, N, d] with H_kv dividing H.  Query head h attends with key/value
+    head h // (H / H_kv) [P4 §18.2.2: in GQA the query heads form groups that
+    share one K/V head; §18.7.1: K and V with fewer heads are broadcast along
+    the head dimension].  Returns O [B, H, N, d] and LSE [B, H, N]."""
+    B, H, N, d = q.shape
+    G = _group(H, k.shape[1])
+    o = np.full((B, H, N, v.shape[-1]), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
+        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal)
+    return o, lse
+
+
+def gqa_backward(q, k, v, do, scale, causal=False, groups=None):
+    """Backward of ``gqa_forward``.  dQ, O, LSE, D per query head as in the
+    ungrouped case; dK and dV of key/value head j are the sums, over the query
+    heads h with h // (H / H_kv) == j, of the gradients that head's attention
+    gives to the shared K and V (the chain rule through the broadcast).
+    ``groups``: optional list of (b, j) key/value heads to compute (with all
+    their query heads); entries outside it stay NaN."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    G = _group(H, Hkv)
+    out = {name: np.full(q.shape, np.nan) for name in ("dq", "o")}
+    out["dk"] = np.full(k.shape, np.nan)
+    out["dv"] = np.full(v.shape, np.nan)
+    out["lse"] = np.full((B, H, N), np.nan)
+    out["D"] = np.full((B, H, N), np.nan)
+    todo = groups if groups is not None else [(b, j) for b in range(B) for j in range(Hkv)]
+    for b, j in todo:
+        out["dk"][b, j] = 0.0
+        out["dv"][b, j] = 0.0
+        for h in range(j * G, (j + 1) * G):
+            dq, dk, dv, o, lse, dvec = head_backward(q[b, h], k[b, j], v[b, j], do[b, h], scale, causal)
+            out["dq"][b, h], out["o"][b, h], out["lse"][b, h], out["D"][b, h] = dq, o, lse, dvec
+            out["dk"][b, j] += dk
+            out["dv"][b, j] += dv
     return out

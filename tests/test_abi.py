@@ -24,6 +24,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for need in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32",
+                 "attn_fwd_gqa", "attn_bwd_gqa",
                  "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
                  "miattn_status_string"):
         assert need in names
@@ -107,3 +108,18 @@ def test_varlen_validation():
     assert lib.attn_fwd_varlen(*base, FAKE, 0, 10, 15, 2, 64, 0.1, 1, NULL, NULL) == -1
     assert lib.attn_fwd_varlen(*base, FAKE, 2, 10, 15, 2, 80, 0.1, 1, NULL, NULL) == -2
     assert lib.attn_fwd_varlen(*base, ctypes.c_void_p((1 << 20) + 2), 2, 10, 15, 2, 64, 0.1, 1, NULL, NULL) == -1
+
+
+def test_grouped_head_validation():
+    lib = _lib()
+    fwd = lambda H, Hkv, d=64: lib.attn_fwd_gqa(*([FAKE] * 5), 1, H, Hkv, 16, d, 0.125, 1, NULL)
+    assert fwd(8, 0) == -1       # no key/value heads
+    assert fwd(8, 3) == -1       # 3 does not divide 8
+    assert fwd(8, 16) == -1      # more key/value heads than query heads
+    assert fwd(0, 1) == -1
+    assert fwd(8, 2, d=96) == -2
+    need = lib.attn_bwd_workspace_bytes(1, 8, 64, 64)
+    bwd = lambda H, Hkv, ws: lib.attn_bwd_gqa(*([FAKE] * 9), 1, H, Hkv, 64, 64, 0.125, 1, FAKE, ws, NULL)
+    assert bwd(8, 3, need) == -1
+    assert bwd(8, 2, need - 4) == -1
+    assert lib.attn_bwd_gqa(*([FAKE] * 8), NULL, 1, 8, 2, 64, 64, 0.125, 1, FAKE, need, NULL) == -1
