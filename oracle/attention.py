@@ -23,6 +23,12 @@ Readings where the pages are loose (each is listed in the design doc):
     LSE is that of the scaled scores and dQ, dK carry one factor of ``scale``.
   * LSE uses the natural logarithm.
   * Causal masking keeps key j for query i iff j <= i, counted within a sequence.
+  * Sliding window (left, right), -1 meaning unbounded on that side: key j is
+    visible to query i iff i - left <= j <= i + right, in addition to any
+    causal or padding mask.
+  * Block-sparse layout: positions are cut into blocks of ``block`` tokens;
+    query block r lists, in CSR form (row_ptr, col_idx), the key blocks it
+    attends; a listed index counts once however often it is listed.
 """
 from __future__ import annotations
 
@@ -39,21 +45,60 @@ __all__ = [
     "varlen_backward",
     "gqa_forward",
     "gqa_backward",
+    "block_table",
 ]
 
 
-def visible_mask(rows: np.ndarray, n_keys: int, causal: bool, key_valid=None) -> np.ndarray:
+def block_table(row_ptr, col_idx, n_qblocks: int, n_kblocks: int) -> np.ndarray:
+    """Boolean [n_qblocks, n_kblocks] from a CSR block list: entry (r, c) is True
+    iff c appears among col_idx[row_ptr[r] : row_ptr[r+1]] [P4 §18.8.1: the
+    preprocessing step stores, for every query block, the key blocks it must
+    compute].  Raises on a malformed list."""
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    if rp.shape != (n_qblocks + 1,) or rp[0] != 0 or np.any(np.diff(rp) < 0) or rp[-1] != len(ci):
+        raise ValueError("row_ptr must be non-decreasing, start at 0 and end at len(col_idx)")
+    if len(ci) and (ci.min() < 0 or ci.max() >= n_kblocks):
+        raise ValueError("col_idx entries must index key blocks")
+    table = np.zeros((n_qblocks, n_kblocks), dtype=bool)
+    for r in range(n_qblocks):
+        table[r, ci[rp[r]:rp[r + 1]]] = True
+    return table
+
+
+def visible_mask(rows: np.ndarray, n_keys: int, causal: bool, key_valid=None, window=None,
+                 blocks=None) -> np.ndarray:
     """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend key j.
 
     Causal: key j is visible to query i iff j <= i [P4 §18.2.2 item 3, M_ij = 0 for
     j <= i].  Key padding: invalid keys are hidden from every query [P4 §18.2.2
-    item 4]."""
+    item 4].  ``window`` = (left, right): key j is visible to query i only if
+    i - left <= j <= i + right, a negative side being unbounded [P4 §18.7.1, the
+    window_size argument; §18.8.1 sliding window].  ``blocks`` = (row_ptr,
+    col_idx, block): key j is visible to query i only if key block j // block is
+    listed for query block i // block [P4 §18.8.1, block-sparse FlashAttention:
+    blocks that are not listed contribute nothing]."""
     rows = np.asarray(rows)
+    keys = np.arange(n_keys)
     vis = np.ones((len(rows), n_keys), dtype=bool)
     if causal:
-        vis &= np.arange(n_keys)[None, :] <= rows[:, None]
+        vis &= keys[None, :] <= rows[:, None]
     if key_valid is not None:
         vis &= np.asarray(key_valid, dtype=bool)[None, :]
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            vis &= keys[None, :] >= rows[:, None] - left
+        if right >= 0:
+            vis &= keys[None, :] <= rows[:, None] + right
+    if blocks is not None:
+        row_ptr, col_idx, block = blocks
+        n_q = len(row_ptr) - 1
+        table = block_table(row_ptr, col_idx, n_q, -(-n_keys // block))
+        rb = rows // block
+        if len(rows) and rb.max() >= n_q:
+            raise ValueError("a query row lies past the last query block of the list")
+        vis &= table[rb][:, keys // block]
     return vis
 
 
@@ -80,12 +125,13 @@ def _row_softmax_and_lse(s):
     return p, lse
 
 
-def head_forward(q, k, v, scale, causal=False, key_valid=None, rows=None, row_chunk=2048):
+def head_forward(q, k, v, scale, causal=False, key_valid=None, rows=None, row_chunk=2048, window=None, blocks=None):
     """O and LSE for one head.  q, k, v: [N, d] (any float dtype, used as fp64).
 
     ``rows`` selects query rows (default: all), which lets a test check sampled
     rows of a large problem; each row is still computed from its full score row.
-    Returns (O [len(rows), d] fp64, LSE [len(rows)] fp64)."""
+    ``window`` / ``blocks``: optional sliding-window and block-sparse masks
+    (see ``visible_mask``).  Returns (O [len(rows), d] fp64, LSE [len(rows)] fp64)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -95,7 +141,7 @@ def head_forward(q, k, v, scale, causal=False, key_valid=None, rows=None, row_ch
     lse = np.zeros(len(rows))
     for c0 in range(0, len(rows), row_chunk):
         r = rows[c0:c0 + row_chunk]
-        s = _scores(q[r], k, scale, visible_mask(r, n_keys, causal, key_valid))
+        s = _scores(q[r], k, scale, visible_mask(r, n_keys, causal, key_valid, window, blocks))
         p, l_ = _row_softmax_and_lse(s)
         o[c0:c0 + len(r)] = p @ v
         lse[c0:c0 + len(r)] = l_
@@ -103,7 +149,7 @@ def head_forward(q, k, v, scale, causal=False, key_valid=None, rows=None, row_ch
 
 
 def head_backward(q, k, v, do, scale, causal=False, key_valid=None, row_chunk=2048,
-                  check_d_identity=True):
+                  check_d_identity=True, window=None, blocks=None):
     """dQ, dK, dV for one head, plus O, LSE and D (all fp64).
 
     P is rebuilt from the definition (not from any saved state), then the
@@ -124,7 +170,7 @@ def head_backward(q, k, v, do, scale, causal=False, key_valid=None, row_chunk=20
     dvec = np.zeros(n)
     for c0 in range(0, n, row_chunk):
         r = np.arange(c0, min(n, c0 + row_chunk))
-        s = _scores(q[r], k, scale, visible_mask(r, n_keys, causal, key_valid))
+        s = _scores(q[r], k, scale, visible_mask(r, n_keys, causal, key_valid, window, blocks))
         p, l_ = _row_softmax_and_lse(s)
         o_r = p @ v
         dp = do[r] @ v.T                      # dP = dO V^T
@@ -145,7 +191,7 @@ def head_backward(q, k, v, do, scale, causal=False, key_valid=None, row_chunk=20
 
 
 def head_backward_sampled(q, k, v, do, scale, causal=False, key_valid=None, query_rows=(), key_cols=(),
-                          row_chunk=2048):
+                          row_chunk=2048, window=None, blocks=None):
     """The backward of one head evaluated only at chosen outputs: dQ at
     ``query_rows`` and dK, dV at ``key_cols`` (plus O, LSE and D for all rows).
 
@@ -158,13 +204,13 @@ def head_backward_sampled(q, k, v, do, scale, causal=False, key_valid=None, quer
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     n, n_keys = q.shape[0], k.shape[0]
-    o, lse = head_forward(q, k, v, scale, causal, key_valid, row_chunk=row_chunk)
+    o, lse = head_forward(q, k, v, scale, causal, key_valid, row_chunk=row_chunk, window=window, blocks=blocks)
     dvec = np.sum(do * o, axis=1)
     rows = np.asarray(query_rows, dtype=np.int64)
     cols = np.asarray(key_cols, dtype=np.int64)
     dq = np.zeros((len(rows), q.shape[1]))
     if len(rows):
-        s = _scores(q[rows], k, scale, visible_mask(rows, n_keys, causal, key_valid))
+        s = _scores(q[rows], k, scale, visible_mask(rows, n_keys, causal, key_valid, window, blocks))
         dead = ~np.isfinite(lse[rows])
         p = np.where(dead[:, None], 0.0, np.exp(s - np.where(dead, 0.0, lse[rows])[:, None]))
         dp = do[rows] @ v.T
@@ -175,7 +221,7 @@ def head_backward_sampled(q, k, v, do, scale, causal=False, key_valid=None, quer
     if len(cols):
         for c0 in range(0, n, row_chunk):
             r = np.arange(c0, min(n, c0 + row_chunk))
-            vis = visible_mask(r, n_keys, causal, key_valid)[:, cols]
+            vis = visible_mask(r, n_keys, causal, key_valid, window, blocks)[:, cols]
             s = np.where(vis, scale * (q[r] @ k[cols].T), -np.inf)
             dead = ~np.isfinite(lse[r])
             p = np.where(dead[:, None], 0.0, np.exp(s - np.where(dead, 0.0, lse[r])[:, None]))
@@ -259,22 +305,24 @@ def _group(H, Hkv):
     return H // Hkv
 
 
-def gqa_forward(q, k, v, scale, causal=False, heads=None):
+def gqa_forward(q, k, v, scale, causal=False, heads=None, window=None, blocks=None):
     """Grouped key/value heads, dense layout: q [B, H, N, d], k and v
     [B, H_kv, N, d] with H_kv dividing H.  Query head h attends with key/value
     head h // (H / H_kv) [P4 §18.2.2: in GQA the query heads form groups that
     share one K/V head; §18.7.1: K and V with fewer heads are broadcast along
-    the head dimension].  Returns O [B, H, N, d] and LSE [B, H, N]."""
+    the head dimension].  ``window`` / ``blocks`` as in ``visible_mask``, the
+    same for every head.  Returns O [B, H, N, d] and LSE [B, H, N]."""
     B, H, N, d = q.shape
     G = _group(H, k.shape[1])
     o = np.full((B, H, N, v.shape[-1]), np.nan)
     lse = np.full((B, H, N), np.nan)
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
-        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal)
+        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal,
+                                          window=window, blocks=blocks)
     return o, lse
 
 
-def gqa_backward(q, k, v, do, scale, causal=False, groups=None):
+def gqa_backward(q, k, v, do, scale, causal=False, groups=None, window=None, blocks=None):
     """Backward of ``gqa_forward``.  dQ, O, LSE, D per query head as in the
     ungrouped case; dK and dV of key/value head j are the sums, over the query
     heads h with h // (H / H_kv) == j, of the gradients that head's attention
@@ -294,7 +342,8 @@ def gqa_backward(q, k, v, do, scale, causal=False, groups=None):
         out["dk"][b, j] = 0.0
         out["dv"][b, j] = 0.0
         for h in range(j * G, (j + 1) * G):
-            dq, dk, dv, o, lse, dvec = head_backward(q[b, h], k[b, j], v[b, j], do[b, h], scale, causal)
+            dq, dk, dv, o, lse, dvec = head_backward(q[b, h], k[b, j], v[b, j], do[b, h], scale, causal,
+                                                     window=window, blocks=blocks)
             out["dq"][b, h], out["o"][b, h], out["lse"][b, h], out["D"][b, h] = dq, o, lse, dvec
             out["dk"][b, j] += dk
             out["dv"][b, j] += dv

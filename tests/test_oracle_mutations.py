@@ -80,8 +80,8 @@ MUTATIONS = [
     ("attention.py", "ds = p * (dp - d_r[:, None])", "ds = p * dp", "dropped D term"),
     ("attention.py", "dp = do[r] @ v.T", "dp = 0.5 * (do[r] @ v.T)", "scaled dP"),
     ("attention.py", "dv += p.T @ do[r]", "dv += p.T @ do[r][:, ::-1]", "transposed operand columns in dV"),
-    ("attention.py", "vis &= np.arange(n_keys)[None, :] <= rows[:, None]", "vis &= np.arange(n_keys)[None, :] < rows[:, None]", "causal diagonal excluded"),
-    ("attention.py", "vis &= np.arange(n_keys)[None, :] <= rows[:, None]", "vis &= np.arange(n_keys)[None, :] >= rows[:, None]", "causal mask inverted"),
+    ("attention.py", "vis &= keys[None, :] <= rows[:, None]\n", "vis &= keys[None, :] < rows[:, None]\n", "causal diagonal excluded"),
+    ("attention.py", "vis &= keys[None, :] <= rows[:, None]\n", "vis &= keys[None, :] >= rows[:, None]\n", "causal mask inverted"),
     ("attention.py", "s = scale * (q_rows @ k.T)", "s = (q_rows @ k.T) / max(scale, 1e-300)", "scale divides"),
     ("attention.py", "lse = np.where(dead, -np.inf, m_safe + np.log(np.where(dead, 1.0, denom)))",
      "lse = np.where(dead, -np.inf, np.log(np.where(dead, 1.0, denom)))", "LSE without max"),
