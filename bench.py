@@ -46,7 +46,50 @@ WORKLOADS = {
     "noncausal_b8_h16_n2048_d64": dict(B=8, H=16, N=2048, d=64, causal=False, sigma_qk=1.0),
     # grouped key/value heads: 32 query heads share 8 K/V heads (groups of 4)
     "gqa_causal_b4_h32_hkv8_n4096_d128": dict(B=4, H=32, Hkv=8, N=4096, d=128, causal=True, sigma_qk=1.0),
+    # causal sliding window of 4096 keys (window (4095, 0)) over 16384 tokens
+    "swa4096_b1_h32_hkv8_n16384_d128": dict(B=1, H=32, Hkv=8, N=16384, d=128, causal=True, sigma_qk=1.0,
+                                             window=(4095, 0)),
+    # block-sparse, 128 x 128 blocks: block 0 (global), r-1, r, r+1 (local), every 16th block (strided)
+    "blocksparse_b1_h32_hkv8_n16384_d128": dict(B=1, H=32, Hkv=8, N=16384, d=128, causal=False, sigma_qk=1.0,
+                                                 blocks="global+local+strided16"),
 }
+SPARSE_BLOCK = 128
+
+
+def block_rows(pattern, nb):
+    """Key blocks listed per query block for a named block-sparse pattern."""
+    if pattern == "global+local+strided16":
+        return [sorted({0} | {c for c in (r - 1, r, r + 1) if 0 <= c < nb} | set(range(0, nb, 16)))
+                for r in range(nb)]
+    raise ValueError(pattern)
+
+
+def visible_pairs(cfg):
+    """Number of (query, key) pairs the mask keeps, per (batch, head)."""
+    import numpy as np
+    N = cfg["N"]
+    i = np.arange(N, dtype=np.int64)
+    if "window" in cfg:
+        left, right = cfg["window"]
+        lo = np.maximum(0, i - left) if left >= 0 else np.zeros_like(i)
+        hi = np.minimum(N - 1, i + right) if right >= 0 else np.full_like(i, N - 1)
+        if cfg["causal"]:
+            hi = np.minimum(hi, i)
+        return int(np.sum(hi - lo + 1))
+    if "blocks" in cfg:
+        nb = -(-N // SPARSE_BLOCK)
+        size = np.minimum(SPARSE_BLOCK, N - np.arange(nb) * SPARSE_BLOCK)
+        total = 0
+        for r, cols in enumerate(block_rows(cfg["blocks"], nb)):
+            for c in cols:
+                if cfg["causal"] and c > r:
+                    continue
+                if cfg["causal"] and c == r:
+                    total += int(size[r]) * (int(size[r]) + 1) // 2
+                else:
+                    total += int(size[r]) * int(size[c])
+        return total
+    return N * (N + 1) // 2 if cfg["causal"] else N * N
 DEFAULT = "causal_b4_h32_n4096_d128"
 METRIC = "attn fwd/bwd TFLOPS + % MFMA bf16 peak, causal B4 H32 N4096 d128, 1 MI355X"
 
@@ -58,6 +101,31 @@ def log(msg):
 def flops(B, H, N, d, causal):
     fwd = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
     return fwd, 2.5 * fwd
+
+
+def workload_flops(cfg):
+    """Forward and backward FLOPs.  Plain workloads use the customary count
+    (N^2 per head, halved under the causal mask); windowed and block-sparse
+    ones count only the (query, key) pairs their mask keeps."""
+    if "window" in cfg or "blocks" in cfg:
+        fwd = 4.0 * cfg["B"] * cfg["H"] * cfg["d"] * visible_pairs(cfg)
+        return fwd, 2.5 * fwd
+    return flops(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"])
+
+
+def oracle_mask(cfg):
+    """The oracle's mask arguments for a workload."""
+    import numpy as np
+    if "window" in cfg:
+        return {"window": cfg["window"]}
+    if "blocks" in cfg:
+        nb = -(-cfg["N"] // SPARSE_BLOCK)
+        rows = block_rows(cfg["blocks"], nb)
+        row_ptr = np.zeros(nb + 1, np.int32)
+        row_ptr[1:] = np.cumsum([len(r) for r in rows])
+        col_idx = np.array([c for r in rows for c in r], np.int32)
+        return {"blocks": (row_ptr, col_idx, SPARSE_BLOCK)}
+    return {}
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_causal_b4_h32_n4096_d128.json")
@@ -101,12 +169,12 @@ def cpu_baseline(inp, cfg, scale, budget_s=10.0):
     while heads < B * H:
         b, h = divmod(heads, H)
         A.head_backward(inp["q"][b, h], inp["k"][b, h // G], inp["v"][b, h // G], inp["do"][b, h], scale,
-                        cfg["causal"])
+                        cfg["causal"], **oracle_mask(cfg))
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    f_fwd, f_bwd = flops(1, 1, N, d, cfg["causal"])
+    f_fwd, f_bwd = workload_flops(dict(cfg, B=1, H=1))
     per_head = dt / heads
     return {
         "value": round(heads * (f_fwd + f_bwd) / dt / 1e12, 6),
@@ -160,7 +228,8 @@ def main(argv=None):
     cfg = WORKLOADS[args.workload]
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
     Hkv = cfg.get("Hkv", H)
-    grouped = Hkv != H
+    masked = "window" in cfg or "blocks" in cfg
+    grouped = Hkv != H or masked   # timed as attn_fwd_* + one backward call
     scale = 1.0 / math.sqrt(d)
     log(f"workload {args.workload}: generating inputs")
     inp = dense_inputs(B, H, N, d, "bf16", seed=0, sigma_qk=cfg["sigma_qk"], kv_heads=Hkv if grouped else None)
@@ -169,16 +238,47 @@ def main(argv=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(M.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ws_bytes = M.attn_bwd_workspace_bytes(B, H, N, d)
+    if "blocks" in cfg:
+        ws_bytes = M.attn_bwd_block_sparse_workspace_bytes(B, H, N, d)
+        mk = oracle_mask(cfg)["blocks"]
+        row_ptr = torch.from_numpy(mk[0]).cuda()
+        col_idx = torch.from_numpy(mk[1]).cuda()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    fwd_name = "attn_fwd_gqa"
+
+    if "window" in cfg:
+        wl, wr = cfg["window"]
+        fwd_name = "attn_fwd_window"
+
+        def fwd_call():
+            M.attn_fwd_window(q, k, v, o, lse, scale, causal, wl, wr, stream)
+
+        def bwd_call():
+            M.attn_bwd_window(q, k, v, o, lse, do, dq, dk, dv, scale, causal, wl, wr, ws, stream)
+    elif "blocks" in cfg:
+        fwd_name = "attn_fwd_block_sparse"
+
+        def fwd_call():
+            M.attn_fwd_block_sparse(q, k, v, o, lse, scale, causal, row_ptr, col_idx, stream)
+
+        def bwd_call():
+            M.attn_bwd_block_sparse(q, k, v, o, lse, do, dq, dk, dv, scale, causal, row_ptr, col_idx, ws, stream)
+    else:
+        def fwd_call():
+            M.attn_fwd_gqa(q, k, v, o, lse, scale, causal, stream)
+
+        def bwd_call():
+            M.attn_bwd_gqa(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
 
     def step_grouped(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        M.attn_fwd_gqa(q, k, v, o, lse, scale, causal, stream)
+        fwd_call()
         if ev is not None:
             ev[1].record(stream)
-        M.attn_bwd_gqa(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
+        bwd_call()
         if ev is not None:
             ev[4].record(stream)
 
@@ -227,7 +327,7 @@ def main(argv=None):
     mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
     med = {k_: statistics.median(v_) for k_, v_ in per.items()}
 
-    f_fwd, f_bwd = flops(B, H, N, d, causal)
+    f_fwd, f_bwd = workload_flops(cfg)
     ms_step = wall * 1e3 / args.steps
     bwd_ms = mean["bwd"]
     f_dkdv, f_dq = 2.0 * f_fwd, 1.5 * f_fwd
@@ -257,12 +357,17 @@ def main(argv=None):
         kern["bwd_dkdv_kernel (attn_bwd_dkdv)"] = (mean["bwd_dkdv"], f_dkdv)
         kern["bwd_dq_kernel (attn_bwd_dq)"] = (mean["bwd_dq"], f_dq)
     else:
-        kern = {"fwd_stag_kernel (attn_fwd_gqa)": (mean["fwd"], f_fwd)}
+        kern = {f"fwd_stag_kernel ({fwd_name})": (mean["fwd"], f_fwd)}
     dom = max(kern, key=lambda k_: kern[k_][0])
     dom_ms, dom_flops = kern[dom]
     dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
 
-    heads = f"H{H}" + (f" H_kv{Hkv}" if grouped else "")
+    heads = f"H{H}" + (f" H_kv{Hkv}" if Hkv != H else "")
+    mask_desc = ""
+    if "window" in cfg:
+        mask_desc = f" window{cfg['window']}"
+    elif "blocks" in cfg:
+        mask_desc = f" block-sparse {cfg['blocks']} ({SPARSE_BLOCK}x{SPARSE_BLOCK} blocks)"
     result = {
         "metric": METRIC if args.workload == DEFAULT else f"attn fwd+bwd TFLOPS, {args.workload}, 1 MI355X",
         "value": round(value, 3),
@@ -276,9 +381,10 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"exact attention fwd+bwd, {'causal' if causal else 'non-causal'} "
+        "config": {"workload": f"exact attention fwd+bwd, {'causal' if causal else 'non-causal'}{mask_desc} "
                                f"B{B} {heads} N{N} d{d} bf16", "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d,
-                   "causal": causal, "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd},
+                   "causal": causal, "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd,
+                   "visible_pairs_per_head": visible_pairs(cfg) if masked else None},
         "fwd": {"ms": round(mean["fwd"], 4), "ms_median": round(med["fwd"], 4), "tflops": round(tflops_fwd, 2),
                 "pct_mfma_peak": round(100 * tflops_fwd / PEAK_BF16_TFLOPS, 2),
                 "gbps": round(fwd_bytes / (mean["fwd"] * 1e-3) / 1e9, 1)},

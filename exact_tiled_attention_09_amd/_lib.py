@@ -37,6 +37,11 @@ SIGNATURES = {
     "attn_bwd_dq": (_I, [_P] * 6 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_gqa": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_fwd_window": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _I, _I, _P]),
+    "attn_bwd_window": (_I, [_P] * 9 + [_I] * 5 + [_F, _I, _I, _I, _P, _S, _P]),
+    "attn_fwd_block_sparse": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _P, _P, _I, _P]),
+    "attn_bwd_block_sparse_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_bwd_block_sparse": (_I, [_P] * 9 + [_I] * 5 + [_F, _I, _P, _P, _I, _P, _S, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_f32": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_varlen": (_I, [_P] * 5 + [_P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
@@ -167,6 +172,47 @@ def attn_bwd_gqa(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, wo
                                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
                                                int(bool(causal)), _ptr(workspace),
                                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_fwd_window(q, k, v, o, lse, scale: float, causal: bool, window_left: int, window_right: int,
+                    stream=None):
+    B, H, Hkv, N, d = _gqa_dims(q, k)
+    _check("attn_fwd_window", load().attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                                     float(scale), int(bool(causal)), int(window_left),
+                                                     int(window_right), _stream(stream)))
+
+
+def attn_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, window_left: int,
+                    window_right: int, workspace, stream=None):
+    B, H, Hkv, N, d = _gqa_dims(q, k)
+    _check("attn_bwd_window", load().attn_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                                     _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
+                                                     int(bool(causal)), int(window_left), int(window_right),
+                                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                     _stream(stream)))
+
+
+def attn_fwd_block_sparse(q, k, v, o, lse, scale: float, causal: bool, row_ptr, col_idx, stream=None):
+    """row_ptr, col_idx: int32 device tensors (the CSR block list)."""
+    B, H, Hkv, N, d = _gqa_dims(q, k)
+    _check("attn_fwd_block_sparse",
+           load().attn_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                        float(scale), int(bool(causal)), _ptr(row_ptr), _ptr(col_idx),
+                                        int(col_idx.numel()), _stream(stream)))
+
+
+def attn_bwd_block_sparse_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().attn_bwd_block_sparse_workspace_bytes(B, H, N, d))
+
+
+def attn_bwd_block_sparse(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, row_ptr, col_idx,
+                          workspace, stream=None):
+    B, H, Hkv, N, d = _gqa_dims(q, k)
+    _check("attn_bwd_block_sparse",
+           load().attn_bwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                                        _ptr(row_ptr), _ptr(col_idx), int(col_idx.numel()), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def attn_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

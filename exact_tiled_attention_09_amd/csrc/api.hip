@@ -53,6 +53,48 @@ int check_varlen(const int* cu, int nseq, int max_seqlen, int total_tokens, int 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP; }
 
+bool groups_ok(int H, int H_kv) { return H_kv > 0 && H > 0 && H % H_kv == 0; }
+
+// Sliding window arguments -> mask mode.  A side of -1 is unbounded; sides
+// are clamped to [0, N]; a causal mask is the right side 0.  A window that
+// restricts nothing runs the plain kernels (mode kMaskPlain, *causal set to
+// whether the result is the causal mask); otherwise a.win_* are set.
+int window_mode(AttnArgs& a, int N, int left, int right, bool* causal, int* mode) {
+  if (left < -1 || right < -1) return MIATTN_ERR_INVALID_ARG;
+  const int L = left < 0 ? N : (left < N ? left : N);
+  int R = right < 0 ? N : (right < N ? right : N);
+  if (*causal) R = 0;
+  if (L >= N - 1 && (R == 0 || R >= N - 1)) {
+    *causal = R == 0 && N > 1;
+    *mode = miattn::kMaskPlain;
+    return MIATTN_OK;
+  }
+  a.win_left = L;
+  a.win_right = R;
+  *causal = false;
+  *mode = miattn::kMaskWindow;
+  return MIATTN_OK;
+}
+
+// Block-sparse list: blocks of MIATTN_SPARSE_BLOCK tokens, one CSR row per
+// query block, shared by every (batch, head).
+int sparse_args(AttnArgs& a, int N, const int* row_ptr, const int* col_idx, int nnz) {
+  if (N > miattn::kMaxSparseBlocks * miattn::kSparseBlock) return MIATTN_ERR_UNSUPPORTED;
+  if (row_ptr == nullptr || !aligned(row_ptr, 4) || nnz < 0) return MIATTN_ERR_INVALID_ARG;
+  if (nnz > 0 && (col_idx == nullptr || !aligned(col_idx, 4))) return MIATTN_ERR_INVALID_ARG;
+  a.blk_row_ptr = row_ptr;
+  a.blk_col_idx = col_idx;
+  a.blk_nnz = nnz;
+  a.n_qblk = (N + miattn::kSparseBlock - 1) / miattn::kSparseBlock;
+  a.n_kblk = a.n_qblk;
+  return MIATTN_OK;
+}
+
+size_t sparse_table_bytes(int N) {
+  const size_t nb = ((size_t)N + miattn::kSparseBlock - 1) / miattn::kSparseBlock;
+  return round_up(nb * nb, 256);
+}
+
 AttnArgs dense_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
                     int N, float scale) {
   AttnArgs a = {};
@@ -172,7 +214,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
                  int d, float scale, int causal, hipStream_t stream) {
   if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
-  if (H_kv <= 0 || H <= 0 || H % H_kv != 0) return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, scale)) return st;
   AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
   a.Hkv = H_kv;
@@ -185,7 +227,7 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
   if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
       !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
     return MIATTN_ERR_INVALID_ARG;
-  if (H_kv <= 0 || H <= 0 || H % H_kv != 0) return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
   if (int st = check_dense(B, H, N, d, scale)) return st;
   const int64_t rows = (int64_t)B * H * N;
   if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
@@ -199,6 +241,95 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
   if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
   if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream))) return st;
   return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                    int d, float scale, int causal, int window_left, int window_right, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.Hkv = H_kv;
+  bool c = causal != 0;
+  int mode = 0;
+  if (int st = window_mode(a, N, window_left, window_right, &c, &mode)) return st;
+  if (mode == miattn::kMaskPlain) return hip_status(miattn::launch_fwd_bf16(a, d, c, false, stream));
+  return hip_status(miattn::launch_fwd_masked_bf16(a, d, mode, false, stream));
+}
+
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                    void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    int window_left, int window_right, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.Hkv = H_kv;
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, workspace, rows);
+  bool c = causal != 0;
+  int mode = 0;
+  if (int st = window_mode(a, N, window_left, window_right, &c, &mode)) return st;
+  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
+  if (mode == miattn::kMaskPlain) {
+    if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, c, false, stream))) return st;
+    return hip_status(miattn::launch_bwd_dq_bf16(a, d, c, false, stream));
+  }
+  if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, mode, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, mode, false, stream));
+}
+
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                          int N, int d, float scale, int causal, const int* row_ptr, const int* col_idx, int nnz,
+                          hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.Hkv = H_kv;
+  if (int st = sparse_args(a, N, row_ptr, col_idx, nnz)) return st;
+  return hip_status(miattn::launch_fwd_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream));
+}
+
+size_t attn_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d) {
+  if (check_dense(B, H, N, d, 1.0f) != MIATTN_OK) return 0;
+  if (N > miattn::kMaxSparseBlocks * miattn::kSparseBlock) return 0;
+  return workspace_bytes_for((int64_t)B * H * N) + sparse_table_bytes(N);
+}
+
+int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dO, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+                          float scale, int causal, const int* row_ptr, const int* col_idx, int nnz, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv) || !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  if (int st = sparse_args(a, N, row_ptr, col_idx, nnz)) return st;
+  if (workspace_bytes < workspace_bytes_for(rows) + sparse_table_bytes(N)) return MIATTN_ERR_INVALID_ARG;
+  a.Hkv = H_kv;
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, workspace, rows);
+  uint8_t* table = static_cast<uint8_t*>(workspace) + workspace_bytes_for(rows);
+  a.blk_table = table;
+  if (int st = hip_status(miattn::launch_block_table(a, table, stream))) return st;
+  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
+  if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream)))
+    return st;
+  return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream));
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,

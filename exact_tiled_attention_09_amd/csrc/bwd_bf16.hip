@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(AttnArgs a, int64_t rows)
 // NW = 8: waves w and w+4 own the same 32 keys and split the query tile by
 // halves, two waves per SIMD; their partial dK/dV are summed through LDS at
 // the end.
-template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_ktiles) {
   constexpr int NT = NW * 64;
   constexpr int BK = 128;            // keys per workgroup (4 blocks of 32)
@@ -147,24 +147,55 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     dv[db] = f32x16{};
   }
 
+  // The query tiles a key tile meets: qt_begin .. qt_begin + nsteps - 1
+  // (from the diagonal on under a causal mask; the run a window allows), or
+  // with a block list both 64-row halves of every 128-row query block that
+  // lists this key block (tile_at(p) = 2 * s_qlist[p / 2] + p % 2).
   const int n_qt = (len + BQ - 1) / BQ;
-  const int qt_begin = CAUSAL ? k0 / BQ : 0;
-  // Steps v = 0 .. nv-1 run query tile qt_begin + v % nsteps of the group's
-  // query head v / nsteps.  The tile and head of the step to fetch next are
-  // kept incrementally (tile nit of the head whose Q / dO start at nq / ng and
-  // whose LSE / D rows start at nrow), so the loop does no division.
-  const int nsteps = n_qt - qt_begin;
+  __shared__ uint16_t s_qlist[MASK == kMaskBlocks ? kMaxSparseBlocks : 1];
+  __shared__ int s_qcount;
+  int qt_begin = 0, nsteps;
+  if constexpr (MASK == kMaskPlain) {
+    qt_begin = CAUSAL ? k0 / BQ : 0;
+    nsteps = n_qt - qt_begin;
+  } else if constexpr (MASK == kMaskWindow) {
+    qt_begin = max(0, k0 - a.win_right) / BQ;
+    nsteps = min(n_qt - 1, (k0 + BK - 1 + a.win_left) / BQ) - qt_begin + 1;
+  } else {
+    static_assert(BK == kSparseBlock && 2 * BQ == kSparseBlock, "one key block per workgroup");
+    nsteps = 2 * build_query_block_list<CAUSAL>(a, kt, s_qlist, &s_qcount);
+  }
+  auto tile_at = [&](int p) __attribute__((always_inline)) -> int {
+    if constexpr (MASK == kMaskBlocks) return 2 * (int)s_qlist[p >> 1] + (p & 1);
+    else return qt_begin + p;
+  };
+  // Steps v = 0 .. nv-1 run list position v % nsteps of the group's query
+  // head v / nsteps.  The tile and head of the step to fetch next are kept
+  // incrementally (tile nit at position npos, of the head whose Q / dO start
+  // at nq / ng and whose LSE / D rows start at nrow), so the loop does no
+  // division.
   const int nv = G * nsteps;
-  int nit = qt_begin;
+  int npos = 0;
+  int nit = tile_at(0);
   const uint16_t* nq = qp;
   const uint16_t* ng = gp;
   int64_t nrow = sv.row_base;
   auto advance = [&]() __attribute__((always_inline)) {
-    if (++nit == n_qt) {
-      nit = qt_begin;
-      nq += qhs;
-      ng += qhs;
-      nrow += rhs;
+    if constexpr (MASK == kMaskBlocks) {
+      if (++npos == nsteps) {
+        npos = 0;
+        nq += qhs;
+        ng += qhs;
+        nrow += rhs;
+      }
+      nit = tile_at(npos);
+    } else {
+      if (++nit == qt_begin + nsteps) {
+        nit = qt_begin;
+        nq += qhs;
+        ng += qhs;
+        nrow += rhs;
+      }
     }
   };
 
@@ -215,151 +246,161 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     }
   };
 
-  // Prologue: the first Q/dO tile in flight, then K and V (rows past the
-  // sequence are zero) and the first LSE/D rows; one wait covers all.
-  issue_tile(0);
+  // A key block no query block lists gets dK = dV = 0.
+  if (MASK != kMaskBlocks || nv > 0) {
+    // Prologue: the first Q/dO tile in flight, then K and V (rows past the
+    // sequence are zero) and the first LSE/D rows; one wait covers all.
+    issue_tile(0);
 #pragma unroll
-  for (int cidx = 0; cidx < KCPT; ++cidx) {
-    const int chunk = tid + cidx * NT;
-    const int row = chunk / CH_PER_ROW;
-    const int col = (chunk - row * CH_PER_ROW) * 8;
-    const int key = k0 + row;
-    const int kc = min(key, len - 1);
-    const uint32_t keep = key < len ? 0xffffffffu : 0u;
-    const u32x4 xk = *(const u32x4*)(kp + (int64_t)kc * sv.kv_stride + col) & keep;
-    const u32x4 xv = *(const u32x4*)(vp + (int64_t)kc * sv.kv_stride + col) & keep;
-    const int off = swz_off<D>(row, col);
-    *(u32x4*)(sK + off) = xk;
-    *(u32x4*)(sV + off) = xv;
-  }
-  load_rows();
-  store_rows(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first Q/dO tile too
-  barrier_vmem_n<0>();
-
-  // Per-lane operand offsets (a row's swizzle depends only on the row mod 16).
-  int aoff[KS];       // b128 operand rows (query or key) l32, chunk 2*ks + hi
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) aoff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
-  const int tr_r = hi * 4 + ((lane >> 2) & 3);
-  const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  int troff[2][DB];   // transpose reads: rows 8R + tr_r, columns db*32 + tr_c
-#pragma unroll
-  for (int R = 0; R < 2; ++R)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
-  const uint16_t* kb_rows = sK + kblk * 32 * D;
-  const uint16_t* vb_rows = sV + kblk * 32 * D;
-
-  // Step v from buffer BUF (= v % 2, a compile-time constant so that every
-  // LDS address is a register plus an immediate).
-  auto step = [&](int v, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    const int it = nit;
-    advance();
-    const int q0 = it * BQ;
-    const bool fetch = v + 1 < nv;
-    if (fetch) load_rows();
-    // The loads of tile it+1 are spread over the first live half's S / dP
-    // MFMAs (all waves issuing together would queue in the CU's memory
-    // pipeline); a wave with no live half issues them at once.
-    bool pending = fetch;
-
-    const uint16_t* q_s = sQb + buf * QT_ELEMS;
-    const uint16_t* g_s = sGb + buf * QT_ELEMS;
-#pragma unroll
-    for (int qq = 0; qq < QHALVES; ++qq) {
-      const int qb = qh0 + qq;
-      __builtin_amdgcn_sched_barrier(0);
-      if (CAUSAL && q0 + qb * 32 + 31 < wk0) continue;  // this half sees none of the wave's keys
-      bool need_mask = (wk0 + 31 >= len) || any_bad_key;
-      if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0 + qb * 32);
-      // S and dP, their four operands read one k-step ahead.
-      f32x16 s = f32x16{}, dp = f32x16{};
-      bf16x8 opq[2], opk[2], opg[2], opv[2];
-      auto sread = [&](int ks, int u) __attribute__((always_inline)) {
-        const int off = qb * 32 * D + aoff[ks];
-        opq[u] = as_bf16x8(*(const u32x4*)(q_s + off));
-        opk[u] = as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks]));
-        opg[u] = as_bf16x8(*(const u32x4*)(g_s + off));
-        opv[u] = as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks]));
-      };
-      sread(0, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) sread(ks + 1, (ks + 1) & 1);
-        s = mfma_bf16(opq[ks & 1], opk[ks & 1], s);
-        dp = mfma_bf16(opg[ks & 1], opv[ks & 1], dp);
-        if (pending) {
-#pragma unroll
-          for (int n = ks * 2 * QCPT / KS; n < (ks + 1) * 2 * QCPT / KS; ++n) issue_part(buf ^ 1, n);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      pending = false;
-      float cc = c;
-      if (need_mask) {
-        // Masked entries get an exponent argument of -inf (exp2 -> 0); the
-        // scale is applied before the select and the exponent then uses
-        // multiplier 1, so a zero or negative scale cannot make 0 * -inf.
-        cc = 1.f;
-        const int key_m = pin_in_branch(key_ok ? my_key : 0x7fffffff);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          bool vis = key_m != 0x7fffffff;
-          if (CAUSAL) vis = vis && (key_m <= q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3));
-          s[r] = vis ? s[r] * c : kNegInf;
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = qb * 32 + g * 8 + hi * 4;
-        const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
-        const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = g * 4 + e;
-          const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lv[e]));
-          s[r] = p;
-          dp[r] = p * (dp[r] - dvv[e]);
-        }
-      }
-      // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA; the
-      // transposed dO / Q operands are read one MFMA pair ahead.
-      bf16x8 pa[2], da[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        pa[t] = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
-                            s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
-        da[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
-                            dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-      }
-      constexpr int NKK = 2 * DB;  // (t, db) pairs
-      bf16x8 opgt[2], opqt[2];
-      auto tread = [&](int i, int u) __attribute__((always_inline)) {
-        const int rbase = (qb * 32 + 16 * (i / DB)) * D;
-        const int db = i % DB;
-        opgt[u] = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]), lds_read_tr16(g_s + rbase + troff[1][db]));
-        opqt[u] = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]), lds_read_tr16(q_s + rbase + troff[1][db]));
-      };
-      tread(0, 0);
-#pragma unroll
-      for (int i = 0; i < NKK; ++i) {
-        if (i + 1 < NKK) tread(i + 1, (i + 1) & 1);
-        dv[i % DB] = mfma_bf16(pa[i / DB], opgt[i & 1], dv[i % DB]);
-        dk[i % DB] = mfma_bf16(da[i / DB], opqt[i & 1], dk[i % DB]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int cidx = 0; cidx < KCPT; ++cidx) {
+      const int chunk = tid + cidx * NT;
+      const int row = chunk / CH_PER_ROW;
+      const int col = (chunk - row * CH_PER_ROW) * 8;
+      const int key = k0 + row;
+      const int kc = min(key, len - 1);
+      const uint32_t keep = key < len ? 0xffffffffu : 0u;
+      const u32x4 xk = *(const u32x4*)(kp + (int64_t)kc * sv.kv_stride + col) & keep;
+      const u32x4 xv = *(const u32x4*)(vp + (int64_t)kc * sv.kv_stride + col) & keep;
+      const int off = swz_off<D>(row, col);
+      *(u32x4*)(sK + off) = xk;
+      *(u32x4*)(sV + off) = xv;
     }
-    __builtin_amdgcn_sched_barrier(0);
+    load_rows();
+    store_rows(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first Q/dO tile too
+    barrier_vmem_n<0>();
 
-    if (pending) issue_tile(buf ^ 1);
-    if (fetch) store_rows(buf ^ 1);
-    barrier_vmem_n<0>();  // the next tile has landed
-  };
-  for (int v = 0; v < nv; v += 2) {
-    step(v, std::integral_constant<int, 0>{});
-    if (v + 1 < nv) step(v + 1, std::integral_constant<int, 1>{});
+    // Per-lane operand offsets (a row's swizzle depends only on the row mod 16).
+    int aoff[KS];       // b128 operand rows (query or key) l32, chunk 2*ks + hi
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aoff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
+    const int tr_r = hi * 4 + ((lane >> 2) & 3);
+    const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+    int troff[2][DB];   // transpose reads: rows 8R + tr_r, columns db*32 + tr_c
+#pragma unroll
+    for (int R = 0; R < 2; ++R)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
+    const uint16_t* kb_rows = sK + kblk * 32 * D;
+    const uint16_t* vb_rows = sV + kblk * 32 * D;
+
+    // Step v from buffer BUF (= v % 2, a compile-time constant so that every
+    // LDS address is a register plus an immediate).
+    auto step = [&](int v, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
+      const int it = nit;
+      advance();
+      const int q0 = it * BQ;
+      const bool fetch = v + 1 < nv;
+      if (fetch) load_rows();
+      // The loads of tile it+1 are spread over the first live half's S / dP
+      // MFMAs (all waves issuing together would queue in the CU's memory
+      // pipeline); a wave with no live half issues them at once.
+      bool pending = fetch;
+
+      const uint16_t* q_s = sQb + buf * QT_ELEMS;
+      const uint16_t* g_s = sGb + buf * QT_ELEMS;
+#pragma unroll
+      for (int qq = 0; qq < QHALVES; ++qq) {
+        const int qb = qh0 + qq;
+        __builtin_amdgcn_sched_barrier(0);
+        if (CAUSAL && q0 + qb * 32 + 31 < wk0) continue;  // this half sees none of the wave's keys
+        if (MASK == kMaskWindow &&
+            (q0 + qb * 32 + 31 + a.win_right < wk0 || q0 + qb * 32 - a.win_left > wk0 + 31))
+          continue;  // the window keeps none of the wave's keys for this half
+        bool need_mask = (wk0 + 31 >= len) || any_bad_key;
+        if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0 + qb * 32);
+        if (MASK == kMaskWindow)
+          need_mask = need_mask || (wk0 < q0 + qb * 32 + 31 - a.win_left) || (wk0 + 31 > q0 + qb * 32 + a.win_right);
+        // S and dP, their four operands read one k-step ahead.
+        f32x16 s = f32x16{}, dp = f32x16{};
+        bf16x8 opq[2], opk[2], opg[2], opv[2];
+        auto sread = [&](int ks, int u) __attribute__((always_inline)) {
+          const int off = qb * 32 * D + aoff[ks];
+          opq[u] = as_bf16x8(*(const u32x4*)(q_s + off));
+          opk[u] = as_bf16x8(*(const u32x4*)(kb_rows + aoff[ks]));
+          opg[u] = as_bf16x8(*(const u32x4*)(g_s + off));
+          opv[u] = as_bf16x8(*(const u32x4*)(vb_rows + aoff[ks]));
+        };
+        sread(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) sread(ks + 1, (ks + 1) & 1);
+          s = mfma_bf16(opq[ks & 1], opk[ks & 1], s);
+          dp = mfma_bf16(opg[ks & 1], opv[ks & 1], dp);
+          if (pending) {
+#pragma unroll
+            for (int n = ks * 2 * QCPT / KS; n < (ks + 1) * 2 * QCPT / KS; ++n) issue_part(buf ^ 1, n);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        pending = false;
+        float cc = c;
+        if (need_mask) {
+          // Masked entries get an exponent argument of -inf (exp2 -> 0); the
+          // scale is applied before the select and the exponent then uses
+          // multiplier 1, so a zero or negative scale cannot make 0 * -inf.
+          cc = 1.f;
+          const int key_m = pin_in_branch(key_ok ? my_key : 0x7fffffff);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            bool vis = key_m != 0x7fffffff;
+            const int qrow = q0 + qb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            if (CAUSAL) vis = vis && (key_m <= qrow);
+            if (MASK == kMaskWindow) vis = vis && key_m >= qrow - a.win_left && key_m <= qrow + a.win_right;
+            s[r] = vis ? s[r] * c : kNegInf;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ql = qb * 32 + g * 8 + hi * 4;
+          const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
+          const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = g * 4 + e;
+            const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lv[e]));
+            s[r] = p;
+            dp[r] = p * (dp[r] - dvv[e]);
+          }
+        }
+        // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA; the
+        // transposed dO / Q operands are read one MFMA pair ahead.
+        bf16x8 pa[2], da[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          pa[t] = pack_bf16x8(s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3],
+                              s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]);
+          da[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                              dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
+        }
+        constexpr int NKK = 2 * DB;  // (t, db) pairs
+        bf16x8 opgt[2], opqt[2];
+        auto tread = [&](int i, int u) __attribute__((always_inline)) {
+          const int rbase = (qb * 32 + 16 * (i / DB)) * D;
+          const int db = i % DB;
+          opgt[u] = join_u32x2(lds_read_tr16(g_s + rbase + troff[0][db]), lds_read_tr16(g_s + rbase + troff[1][db]));
+          opqt[u] = join_u32x2(lds_read_tr16(q_s + rbase + troff[0][db]), lds_read_tr16(q_s + rbase + troff[1][db]));
+        };
+        tread(0, 0);
+#pragma unroll
+        for (int i = 0; i < NKK; ++i) {
+          if (i + 1 < NKK) tread(i + 1, (i + 1) & 1);
+          dv[i % DB] = mfma_bf16(pa[i / DB], opgt[i & 1], dv[i % DB]);
+          dk[i % DB] = mfma_bf16(da[i / DB], opqt[i & 1], dk[i % DB]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      if (pending) issue_tile(buf ^ 1);
+      if (fetch) store_rows(buf ^ 1);
+      barrier_vmem_n<0>();  // the next tile has landed
+    };
+    for (int v = 0; v < nv; v += 2) {
+      step(v, std::integral_constant<int, 0>{});
+      if (v + 1 < nv) step(v + 1, std::integral_constant<int, 1>{});
+    }
   }
 
   if constexpr (NW == 8) {
@@ -410,7 +451,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
 // direct-load form); before the barrier that ends tile j each wave waits only
 // for its own loads of tile j+1.  Rows past the sequence repeat its last row
 // and are masked.
-template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD>
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qtiles) {
   constexpr int BC = 64;                 // keys per tile
   constexpr int BR = NW * 32;            // query rows per workgroup
@@ -456,8 +497,41 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
   const int kv_len = sv.len;
-  const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  // Key tiles visited, as a list (the forward's schedule): position r holds
+  // key tile tile_of(r); a wave computes the positions wave_live accepts.
+  __shared__ uint8_t s_bflag[2][MASK == kMaskBlocks ? kMaxSparseBlocks : 1];
+  __shared__ uint16_t s_blist[MASK == kMaskBlocks ? kMaxSparseBlocks : 1];
+  __shared__ int s_bcount;
+  int ntiles, jt0 = 0, jw_first = 0, jw_last = 0;
+  if constexpr (MASK == kMaskPlain) {
+    const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
+    ntiles = (kv_end + BC - 1) / BC;
+  } else if constexpr (MASK == kMaskWindow) {
+    jt0 = max(0, q_tile0 - a.win_left) / BC;
+    const int kv_end = min(kv_len, q_tile0 + BR + a.win_right);
+    ntiles = (kv_end + BC - 1) / BC - jt0;
+    jw_first = max(0, q_wave0 - a.win_left) / BC - jt0;
+    jw_last = min(ntiles - 1, (q_wave0 + 31 + a.win_right) / BC - jt0);
+  } else {
+    static_assert(BR == 2 * kSparseBlock, "two query blocks per workgroup");
+    ntiles = 2 * build_key_block_list<NT, CAUSAL>(a, q_tile0, s_bflag, s_blist, &s_bcount);
+  }
+  auto tile_of = [&](int r) __attribute__((always_inline)) -> int {
+    if constexpr (MASK == kMaskPlain) return r;
+    else if constexpr (MASK == kMaskWindow) return jt0 + r;
+    else return (s_blist[r >> 1] & 0xfff) * 2 + (r & 1);
+  };
+  auto wave_live = [&](int r) __attribute__((always_inline)) -> bool {
+    if constexpr (MASK == kMaskWindow) {
+      return r >= jw_first && r <= jw_last;
+    } else if constexpr (MASK == kMaskBlocks) {
+      const int e = s_blist[r >> 1];
+      const int kt0 = ((e & 0xfff) * 2 + (r & 1)) * BC;
+      return ((e >> (12 + (wave >> 2))) & 1) != 0 && kt0 < kv_len && (!CAUSAL || kt0 <= q_wave0 + 31);
+    } else {
+      return !CAUSAL || r * BC <= q_wave0 + 31;
+    }
+  };
 
   int src_row[LPT], src_col[LPT];
 #pragma unroll
@@ -471,7 +545,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   // for odd n, chunk n / 2.
   auto issue_part = [&](int j, int n) {
     const int i = n >> 1;
-    const int key = min(j * BC + src_row[i], kv_len - 1);
+    const int key = min(tile_of(j) * BC + src_row[i], kv_len - 1);
     const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
     if (n & 1) lds_dma16(vp + off, sV[j % 3] + (i * NT + wave * 64) * 8);
     else lds_dma16(kp + off, sK[j % 3] + (i * NT + wave * 64) * 8);
@@ -514,132 +588,138 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
 #pragma unroll
     for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
 
-  // Prologue: start tiles 0 and 1, then load this wave's Q, dO, LSE and D
-  // rows; one wait (which the compiler sees, so the loop waits for none of
-  // these loads again) covers all of them.
-  load_flags(0);
-  store_flags(0);
-  if (ntiles > 1) {
-    load_flags(1);
-    store_flags(1);
-  }
-  issue(0);
-  if (ntiles > 1) issue(1);
-  // Q and dO as B operands (lane = query, 8 features per k-step).  Rows past
-  // the sequence load its last row and are zeroed (no branch).
-  const int qc = min(qi, sv.len - 1);
-  const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+  // An empty block list leaves dQ = 0.
+  if (MASK != kMaskBlocks || ntiles > 0) {
+    // Prologue: start tiles 0 and 1, then load this wave's Q, dO, LSE and D
+    // rows; one wait (which the compiler sees, so the loop waits for none of
+    // these loads again) covers all of them.
+    load_flags(0);
+    store_flags(0);
+    if (ntiles > 1) {
+      load_flags(1);
+      store_flags(1);
+    }
+    issue(0);
+    if (ntiles > 1) issue(1);
+    // Q and dO as B operands (lane = query, 8 features per k-step).  Rows past
+    // the sequence load its last row and are zeroed (no branch).
+    const int qc = min(qi, sv.len - 1);
+    const uint32_t keep = row_ok ? 0xffffffffu : 0u;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int64_t off = (int64_t)qc * sv.tok_stride + ks * 16 + hi * 8;
-    qf[ks] = as_bf16x8(*(const u32x4*)(qp + off) & keep);
-    gf[ks] = as_bf16x8(*(const u32x4*)(gp + off) & keep);
-  }
-  // a dead or out-of-range row gets P = 0
-  const float lse_raw = a.lse[sv.row_base + qc];
-  const float lse2 = (!row_ok || lse_raw == kNegInf) ? kPosInf : lse_raw * kLog2e;
-  const float dd = row_ok ? a.dvec[sv.row_base + qc] : 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      const int64_t off = (int64_t)qc * sv.tok_stride + ks * 16 + hi * 8;
+      qf[ks] = as_bf16x8(*(const u32x4*)(qp + off) & keep);
+      gf[ks] = as_bf16x8(*(const u32x4*)(gp + off) & keep);
+    }
+    // a dead or out-of-range row gets P = 0
+    const float lse_raw = a.lse[sv.row_base + qc];
+    const float lse2 = (!row_ok || lse_raw == kNegInf) ? kPosInf : lse_raw * kLog2e;
+    const float dd = row_ok ? a.dvec[sv.row_base + qc] : 0.f;
 
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  barrier_vmem_n<0>();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    barrier_vmem_n<0>();
 
-  // One key tile from buffer slot BUF (= j % 3, a compile-time constant).
-  auto step = [&](int j, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    const bool fetch = j + 2 < ntiles;
-    const int kt0 = j * BC;
-    const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
-    if (fetch) load_flags(j + 2);
-    // A wave with work spreads its loads of tile j+2 over the first block's
-    // S^T / dP^T MFMAs; an idle wave issues them at once.
-    if (fetch && !wave_live) issue(j + 2);
-    if (wave_live) {
-      const uint16_t* sk = sK[buf];
-      const uint16_t* svv = sV[buf];
-      bool need_mask = kt0 + BC > kv_len;
-      if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
-      if (KPAD) need_mask = need_mask || (s_anypad[buf] != 0u);
+    // One key tile from buffer slot BUF (= j % 3, a compile-time constant).
+    auto step = [&](int j, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
+      const bool fetch = j + 2 < ntiles;
+      const int kt0 = tile_of(j) * BC;
+      const bool live = wave_live(j);
+      if (fetch) load_flags(j + 2);
+      // A wave with work spreads its loads of tile j+2 over the first block's
+      // S^T / dP^T MFMAs; an idle wave issues them at once.
+      if (fetch && !live) issue(j + 2);
+      if (live) {
+        const uint16_t* sk = sK[buf];
+        const uint16_t* svv = sV[buf];
+        bool need_mask = kt0 + BC > kv_len;
+        if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
+        if (KPAD) need_mask = need_mask || (s_anypad[buf] != 0u);
+        if (MASK == kMaskWindow)
+          need_mask = need_mask || (kt0 < q_wave0 + 31 - a.win_left) || (kt0 + BC - 1 > q_wave0 + a.win_right);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (CAUSAL && kt0 + kb * 32 > q_wave0 + 31) continue;  // block wholly above the diagonal
-        // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query column).
-        // K and V operands read two k-steps ahead of their MFMAs.
-        f32x16 s = f32x16{}, dp = f32x16{};
-        bf16x8 opk[3], opv[3];
-        auto sread = [&](int ks, int u) __attribute__((always_inline)) {
-          opk[u] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
-          opv[u] = as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks]));
-        };
-        sread(0, 0);
-        sread(1, 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 2 < KS) sread(ks + 2, (ks + 2) % 3);
-          s = mfma_bf16(opk[ks % 3], qf[ks], s);
-          dp = mfma_bf16(opv[ks % 3], gf[ks], dp);
-          if (kb == 0 && fetch) {  // block 0 is never skipped when the wave is live
-#pragma unroll
-            for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + 2, n);
-          }
+        for (int kb = 0; kb < 2; ++kb) {
           __builtin_amdgcn_sched_barrier(0);
-        }
-        float cc = c;
-        if (need_mask) {
-          // Masked entries get an exponent argument of -inf (exp2 -> 0),
-          // with the scale applied before the select (see the key-tile pass).
-          cc = 1.f;
-          const int q_m = pin_in_branch(qi);
+          if (CAUSAL && kt0 + kb * 32 > q_wave0 + 31) continue;  // block wholly above the diagonal
+          // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query column).
+          // K and V operands read two k-steps ahead of their MFMAs.
+          f32x16 s = f32x16{}, dp = f32x16{};
+          bf16x8 opk[3], opv[3];
+          auto sread = [&](int ks, int u) __attribute__((always_inline)) {
+            opk[u] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
+            opv[u] = as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks]));
+          };
+          sread(0, 0);
+          sread(1, 1);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS) sread(ks + 2, (ks + 2) % 3);
+            s = mfma_bf16(opk[ks % 3], qf[ks], s);
+            dp = mfma_bf16(opv[ks % 3], gf[ks], dp);
+            if (kb == 0 && fetch) {  // block 0 is never skipped when the wave is live
+#pragma unroll
+              for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + 2, n);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          float cc = c;
+          if (need_mask) {
+            // Masked entries get an exponent argument of -inf (exp2 -> 0),
+            // with the scale applied before the select (see the key-tile pass).
+            cc = 1.f;
+            const int q_m = pin_in_branch(qi);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+              const int key = kt0 + kl;
+              bool vis = key < kv_len;
+              if (CAUSAL) vis = vis && key <= q_m;
+              if (KPAD) vis = vis && s_valid[buf][kl] != 0;
+              if (MASK == kMaskWindow) vis = vis && key >= q_m - a.win_left && key <= q_m + a.win_right;
+              s[r] = vis ? s[r] * c : kNegInf;
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            const int key = kt0 + kl;
-            bool vis = key < kv_len;
-            if (CAUSAL) vis = vis && key <= q_m;
-            if (KPAD) vis = vis && s_valid[buf][kl] != 0;
-            s[r] = vis ? s[r] * c : kNegInf;
+            const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lse2));
+            dp[r] = p * (dp[r] - dd);
+          }
+          // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read,
+          // three MFMAs ahead.
+          bf16x8 dsb[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            dsb[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
+                                 dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
+          constexpr int NKK = 2 * DB;
+          constexpr int PF = 3;
+          auto tread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+            const uint16_t* kt = sk + (kb * 32 + 16 * (i / DB)) * D;
+            return join_u32x2(lds_read_tr16(kt + troff[0][i % DB]), lds_read_tr16(kt + troff[1][i % DB]));
+          };
+          bf16x8 ka[NKK];
+#pragma unroll
+          for (int i = 0; i < PF; ++i) ka[i] = tread(i);
+#pragma unroll
+          for (int i = 0; i < NKK; ++i) {
+            if (i + PF < NKK) ka[i + PF] = tread(i + PF);
+            dq[i % DB] = mfma_bf16(ka[i], dsb[i / DB], dq[i % DB]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lse2));
-          dp[r] = p * (dp[r] - dd);
-        }
-        // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read,
-        // three MFMAs ahead.
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          dsb[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
-                               dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-        constexpr int NKK = 2 * DB;
-        constexpr int PF = 3;
-        auto tread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-          const uint16_t* kt = sk + (kb * 32 + 16 * (i / DB)) * D;
-          return join_u32x2(lds_read_tr16(kt + troff[0][i % DB]), lds_read_tr16(kt + troff[1][i % DB]));
-        };
-        bf16x8 ka[NKK];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) ka[i] = tread(i);
-#pragma unroll
-        for (int i = 0; i < NKK; ++i) {
-          if (i + PF < NKK) ka[i + PF] = tread(i + PF);
-          dq[i % DB] = mfma_bf16(ka[i], dsb[i / DB], dq[i % DB]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
 
-    if (fetch) store_flags(j + 2);
-    // this wave's loads of tile j + 1 have landed (those of j + 2 may not)
-    if (fetch) barrier_vmem_n<2 * LPT>();
-    else barrier_vmem_n<0>();
-  };
-  for (int j = 0; j < ntiles; j += 3) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
-    if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
+      if (fetch) store_flags(j + 2);
+      // this wave's loads of tile j + 1 have landed (those of j + 2 may not)
+      if (fetch) barrier_vmem_n<2 * LPT>();
+      else barrier_vmem_n<0>();
+    };
+    for (int j = 0; j < ntiles; j += 3) {
+      step(j, std::integral_constant<int, 0>{});
+      if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
+      if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers = features).
@@ -684,13 +764,18 @@ static int dkdv_waves() {
   return nw;
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BK = 128;
   const int n_ktiles = (a.N + BK - 1) / BK;
   const int64_t blocks = (int64_t)n_ktiles * a.B * a.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if constexpr (MASK != kMaskPlain) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8, CAUSAL, VARLEN, KPAD, MASK>), dim3((unsigned)blocks), dim3(512), 0,
+                       stream, a, n_ktiles);
+    return hipGetLastError();
+  }
   if (dkdv_waves() == 4)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
                        n_ktiles);
@@ -700,7 +785,7 @@ static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD>
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 static hipError_t launch_dq_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int NW = 8;
   constexpr int BR = NW * 32;
@@ -708,8 +793,8 @@ static hipError_t launch_dq_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
-                     a, n_qtiles);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL, VARLEN, KPAD, MASK>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     stream, a, n_qtiles);
   return hipGetLastError();
 }
 
@@ -736,6 +821,53 @@ hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool causal, bool varlen
   if (d == 128) return dispatch_bwd<128, true>(a, causal, varlen, kpad, stream);
   if (d == 64) return dispatch_bwd<64, true>(a, causal, varlen, kpad, stream);
   return hipErrorInvalidValue;
+}
+
+// Dense layout with a sliding window (causal folded into the window) or a
+// block-sparse list.
+template <bool DQ>
+static hipError_t dispatch_bwd_masked(const AttnArgs& a, int d, int mask, bool causal, hipStream_t s) {
+#define MIATTN_BWD_MASKED(D_, C, M) (DQ ? launch_dq_t<D_, C, false, false, M>(a, s) \
+                                        : launch_dkdv_t<D_, C, false, false, M>(a, s))
+  if (mask == kMaskWindow) {
+    if (d == 128) return MIATTN_BWD_MASKED(128, false, kMaskWindow);
+    if (d == 64) return MIATTN_BWD_MASKED(64, false, kMaskWindow);
+  } else if (mask == kMaskBlocks) {
+    if (d == 128) return causal ? MIATTN_BWD_MASKED(128, true, kMaskBlocks) : MIATTN_BWD_MASKED(128, false, kMaskBlocks);
+    if (d == 64) return causal ? MIATTN_BWD_MASKED(64, true, kMaskBlocks) : MIATTN_BWD_MASKED(64, false, kMaskBlocks);
+  }
+  return hipErrorInvalidValue;
+#undef MIATTN_BWD_MASKED
+}
+
+hipError_t launch_bwd_dkdv_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream) {
+  return dispatch_bwd_masked<false>(a, d, mask, causal, stream);
+}
+
+hipError_t launch_bwd_dq_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream) {
+  return dispatch_bwd_masked<true>(a, d, mask, causal, stream);
+}
+
+// One workgroup per query block r: clears row r of the table, then marks the
+// key blocks listed for r.  Entries past blk_nnz and out-of-range indices
+// are ignored, as in the kernels that read the list directly.
+__global__ void __launch_bounds__(256) block_table_kernel(AttnArgs a, uint8_t* table) {
+  const int r = blockIdx.x;
+  uint8_t* row = table + (int64_t)r * a.n_kblk;
+  for (int c = threadIdx.x; c < a.n_kblk; c += 256) row[c] = 0;
+  __syncthreads();
+  const int e0 = min(max(a.blk_row_ptr[r], 0), a.blk_nnz);
+  const int e1 = min(max(a.blk_row_ptr[r + 1], e0), a.blk_nnz);
+  for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) {
+    const int c = a.blk_col_idx[e];
+    if (c >= 0 && c < a.n_kblk) row[c] = 1;
+  }
+}
+
+hipError_t launch_block_table(const AttnArgs& a, uint8_t* table, hipStream_t stream) {
+  if (a.n_qblk <= 0 || a.n_kblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(block_table_kernel, dim3((unsigned)a.n_qblk), dim3(256), 0, stream, a, table);
+  return hipGetLastError();
 }
 
 }  // namespace miattn

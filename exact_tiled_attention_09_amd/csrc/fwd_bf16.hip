@@ -326,7 +326,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
 // 4-7 (the partner of wave w on its SIMD is w + 4), 1 = odd waves.  The loop
 // is unrolled by the three buffers so that every LDS address is a register
 // plus an immediate.
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE>
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE, int MASK = kMaskPlain>
 __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtiles) {
   constexpr int NW = 8;
   constexpr int BC = 64;
@@ -384,10 +384,48 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = kNegInf, l = 0.f;
 
-  const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
-  const int ntiles = (kv_end + BC - 1) / BC;
-  // the last key tile holding a key this wave may see
-  const int jw_last = CAUSAL ? min(ntiles - 1, (q_wave0 + 31) / BC) : ntiles - 1;
+  // The key tiles the workgroup visits form a list: position r holds key
+  // tile tile_of(r).  Without a window or a block list it is 0 .. ntiles-1
+  // (under a causal mask it ends at the diagonal); a window visits one
+  // contiguous run; a block list visits both 64-key halves of every listed
+  // 128-key block.  A wave computes only the positions wave_live accepts and
+  // otherwise keeps pace with the others (loads and barriers).
+  __shared__ uint8_t s_bflag[2][MASK == kMaskBlocks ? kMaxSparseBlocks : 1];
+  __shared__ uint16_t s_blist[MASK == kMaskBlocks ? kMaxSparseBlocks : 1];
+  __shared__ int s_bcount;
+  int ntiles, jw_last, jt0 = 0, jw_first = 0;
+  if constexpr (MASK == kMaskPlain) {
+    const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
+    ntiles = (kv_end + BC - 1) / BC;
+    // the last key tile holding a key this wave may see
+    jw_last = CAUSAL ? min(ntiles - 1, (q_wave0 + 31) / BC) : ntiles - 1;
+  } else if constexpr (MASK == kMaskWindow) {
+    jt0 = max(0, q_tile0 - a.win_left) / BC;
+    const int kv_end = min(kv_len, q_tile0 + BR + a.win_right);
+    ntiles = (kv_end + BC - 1) / BC - jt0;
+    jw_first = max(0, q_wave0 - a.win_left) / BC - jt0;
+    jw_last = min(ntiles - 1, (q_wave0 + 31 + a.win_right) / BC - jt0);
+  } else {
+    static_assert(BR == 2 * kSparseBlock, "two query blocks per workgroup");
+    ntiles = 2 * build_key_block_list<NT, CAUSAL>(a, q_tile0, s_bflag, s_blist, &s_bcount);
+    jw_last = ntiles - 1;
+  }
+  auto tile_of = [&](int r) __attribute__((always_inline)) -> int {
+    if constexpr (MASK == kMaskPlain) return r;
+    else if constexpr (MASK == kMaskWindow) return jt0 + r;
+    else return (s_blist[r >> 1] & 0xfff) * 2 + (r & 1);
+  };
+  auto wave_live = [&](int r) __attribute__((always_inline)) -> bool {
+    if constexpr (MASK == kMaskWindow) {
+      return r >= jw_first && r <= jw_last;
+    } else if constexpr (MASK == kMaskBlocks) {
+      const int e = s_blist[r >> 1];
+      const int kt0 = ((e & 0xfff) * 2 + (r & 1)) * BC;
+      return ((e >> (12 + (wave >> 2))) & 1) != 0 && kt0 < kv_len && (!CAUSAL || kt0 <= q_wave0 + 31);
+    } else {
+      return true;
+    }
+  };
 
   // Direct-load sources: LDS chunk p = i*NT + tid of a tile holds row p / CPR,
   // logical chunk (p % CPR) ^ swz(row).  Rows past the sequence repeat its
@@ -401,9 +439,10 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
   auto issue = [&](const uint16_t* src, uint16_t* dst, int j) __attribute__((always_inline)) {
+    const int k0 = tile_of(j) * BC;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int key = min(j * BC + src_row[i], kv_len - 1);
+      const int key = min(k0 + src_row[i], kv_len - 1);
       lds_dma16(src + (int64_t)key * sv.kv_stride + src_col[i], dst + (i * NT + wave * 64) * 8);
     }
   };
@@ -484,10 +523,12 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   };
   // The VALU block for tile j.
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int kt0 = j * BC;
+    const int kt0 = tile_of(j) * BC;
     bool need_mask = kt0 + BC > kv_len;
     if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
     if (KPAD) need_mask = need_mask || (s_anypad[j & 3] != 0u);
+    if (MASK == kMaskWindow)
+      need_mask = need_mask || (kt0 < q_wave0 + 31 - a.win_left) || (kt0 + BC - 1 > q_wave0 + a.win_right);
     float cc = c;
     if (need_mask) {
       // Scale first, then hide masked entries as -inf; afterwards the
@@ -503,6 +544,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
           bool vis = key < kv_len;
           if (CAUSAL) vis = vis && key <= qi;
           if (KPAD) vis = vis && s_valid[j & 3][kl] != 0;
+          if (MASK == kMaskWindow) vis = vis && key >= qi - a.win_left && key <= qi + a.win_right;
           s[kb][r] = vis ? s[kb][r] * c : kNegInf;
         }
     }
@@ -558,35 +600,45 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     begin_interval(t + 1);
   };
 
-  // Prologue: K_0, K_1, V_0 and the flags of tiles 0 and 1.
-  load_flags(0);
-  store_flags(0);
-  issue(kp, sK[0], 0);
-  if (ntiles > 1) {
-    load_flags(1);
-    store_flags(1);
-    issue(kp, sK[1], 1);
-  }
-  issue(vp, sV[0], 0);
-  if (ntiles > 1) barrier_vmem_n<2 * LPT>();  // K_0 has landed
-  else barrier_vmem_n<LPT>();
-  begin_interval(0);
+  // An empty block list leaves every row without a key (O = 0, LSE = -inf).
+  if (MASK != kMaskBlocks || ntiles > 0) {
+    // Prologue: K_0, K_1, V_0 and the flags of tiles 0 and 1.
+    load_flags(0);
+    store_flags(0);
+    issue(kp, sK[0], 0);
+    if (ntiles > 1) {
+      load_flags(1);
+      store_flags(1);
+      issue(kp, sK[1], 1);
+    }
+    issue(vp, sV[0], 0);
+    if (ntiles > 1) barrier_vmem_n<2 * LPT>();  // K_0 has landed
+    else barrier_vmem_n<LPT>();
+    begin_interval(0);
 
-  // Every wave passes ntiles + 1 barriers after the prologue: one per key
-  // tile it works on, then the remaining intervals up to ntiles.
-  auto body = [&](int j, auto slot_c) __attribute__((always_inline)) {
-    mma_s(slot_c);
-    if (late) end_interval(j);
-    softmax(j);
-    if (!late) end_interval(j);
-    mma_pv(slot_c);
-  };
-  for (int j = 0; j <= jw_last; j += 3) {
-    body(j, std::integral_constant<int, 0>{});
-    if (j + 1 <= jw_last) body(j + 1, std::integral_constant<int, 1>{});
-    if (j + 2 <= jw_last) body(j + 2, std::integral_constant<int, 2>{});
+    // Every wave passes ntiles + 1 barriers after the prologue: one per key
+    // tile it works on or skips, then the remaining intervals up to ntiles.
+    auto body = [&](int j, auto slot_c) __attribute__((always_inline)) {
+      if constexpr (MASK != kMaskPlain) {
+        if (!wave_live(j)) {
+          end_interval(j);
+          return;
+        }
+      }
+      mma_s(slot_c);
+      if (late) end_interval(j);
+      softmax(j);
+      if (!late) end_interval(j);
+      mma_pv(slot_c);
+    };
+    const int j_end = MASK == kMaskPlain ? jw_last : ntiles - 1;
+    for (int j = 0; j <= j_end; j += 3) {
+      body(j, std::integral_constant<int, 0>{});
+      if (j + 1 <= j_end) body(j + 1, std::integral_constant<int, 1>{});
+      if (j + 2 <= j_end) body(j + 2, std::integral_constant<int, 2>{});
+    }
+    for (int t = j_end + 1; t <= ntiles; ++t) end_interval(t);
   }
-  for (int t = jw_last + 1; t <= ntiles; ++t) end_interval(t);
 
   // Epilogue: O = O~ / l, LSE = ln 2 * (m + log2 l); a row that saw no
   // visible key gets O = 0 and LSE = -inf.
@@ -934,15 +986,15 @@ static hipError_t dispatch_fwd_dma(const AttnArgs& a, bool causal, bool varlen, 
                 : launch_fwd_dma_t<D, NW, NBUF, false, false, false>(a, s);
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE>
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE, int MASK = kMaskPlain>
 static hipError_t launch_fwd_stag_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BR = 8 * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_stag_kernel<D, CAUSAL, VARLEN, KPAD, ROLE>), dim3((unsigned)blocks), dim3(512), 0, stream,
-                     a, n_qtiles);
+  hipLaunchKernelGGL((fwd_stag_kernel<D, CAUSAL, VARLEN, KPAD, ROLE, MASK>), dim3((unsigned)blocks), dim3(512), 0,
+                     stream, a, n_qtiles);
   return hipGetLastError();
 }
 
@@ -1018,6 +1070,23 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, h
     if (t == 5) return dispatch_fwd_dma<64, 4, 2>(a, causal, varlen, kpad, stream);
     if (t == 6) return dispatch_fwd_dma<64, 8, 4>(a, causal, varlen, kpad, stream);
     return dispatch_fwd_stag<64, 0>(a, causal, varlen, kpad, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Dense layout with a sliding window (causal folded into the window) or a
+// block-sparse list (with or without the causal mask): the staggered form.
+hipError_t launch_fwd_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream) {
+  if (mask == kMaskWindow) {
+    if (d == 128) return launch_fwd_stag_t<128, false, false, false, 0, kMaskWindow>(a, stream);
+    if (d == 64) return launch_fwd_stag_t<64, false, false, false, 0, kMaskWindow>(a, stream);
+  } else if (mask == kMaskBlocks) {
+    if (d == 128)
+      return causal ? launch_fwd_stag_t<128, true, false, false, 0, kMaskBlocks>(a, stream)
+                    : launch_fwd_stag_t<128, false, false, false, 0, kMaskBlocks>(a, stream);
+    if (d == 64)
+      return causal ? launch_fwd_stag_t<64, true, false, false, 0, kMaskBlocks>(a, stream)
+                    : launch_fwd_stag_t<64, false, false, false, 0, kMaskBlocks>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -60,7 +60,27 @@ struct AttnArgs {
   int total_tokens;
   float scale;     // multiplies Q K^T
   float scale_log2;  // scale * log2(e)
+  // Sliding window (kernels with the window mask): key j is visible to query
+  // i iff i - win_left <= j <= i + win_right; both are in [0, N] (the host
+  // maps an unbounded side to N and folds a causal mask into win_right = 0).
+  int win_left;
+  int win_right;
+  // Block-sparse list (kernels with the block mask): query block r attends
+  // the key blocks blk_col_idx[blk_row_ptr[r] .. blk_row_ptr[r+1]), blocks of
+  // kSparseBlock tokens; blk_table[r * n_kblk + c] != 0 is the same list
+  // expanded (built for the backward key-tile pass).
+  const int* blk_row_ptr;
+  const int* blk_col_idx;
+  int blk_nnz;     // length of blk_col_idx: entries past it are never read
+  int n_qblk;
+  int n_kblk;
+  const uint8_t* blk_table;
 };
+
+// Mask modes of the kernels besides none / causal.
+enum : int { kMaskPlain = 0, kMaskWindow = 1, kMaskBlocks = 2 };
+constexpr int kSparseBlock = 128;       // tokens per block of a block-sparse list
+constexpr int kMaxSparseBlocks = 1024;  // blocks per sequence (N <= 131072)
 
 // Where one (sequence, query head) lives, and the key/value head it reads.
 struct SeqView {
@@ -260,6 +280,80 @@ __device__ __forceinline__ void barrier_vmem_n() {
 
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// Block-sparse lists in LDS.  A workgroup of query tile rows
+// [q_tile0, q_tile0 + 2 * kSparseBlock) gathers the key blocks listed for its
+// two query blocks into list[0 .. count): entry = block | (bits << 12), bit h
+// set when query block h of the two lists it.  Out-of-range indices and
+// entries past blk_nnz are ignored; a block listed twice counts once; under a
+// causal mask blocks wholly above a query block's diagonal are dropped.  Every
+// thread of the workgroup calls it (it holds barriers); returns count.
+template <int NT, bool CAUSAL>
+__device__ __forceinline__ int build_key_block_list(const AttnArgs& a, int q_tile0,
+                                                    uint8_t (*flag)[kMaxSparseBlocks], uint16_t* list,
+                                                    int* count_slot) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < a.n_kblk; i += NT) {
+    flag[0][i] = 0;
+    flag[1][i] = 0;
+  }
+  __syncthreads();
+  const int qb0 = q_tile0 / kSparseBlock;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int qb = qb0 + hb;
+    if (qb < a.n_qblk) {
+      const int e0 = min(max(a.blk_row_ptr[qb], 0), a.blk_nnz);
+      const int e1 = min(max(a.blk_row_ptr[qb + 1], e0), a.blk_nnz);
+      for (int e = e0 + tid; e < e1; e += NT) {
+        const int c = a.blk_col_idx[e];
+        if (c >= 0 && c < a.n_kblk && (!CAUSAL || c <= qb)) flag[hb][c] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    int count = 0;
+    for (int base = 0; base < a.n_kblk; base += 64) {
+      const int c = base + lane;
+      const int f = c < a.n_kblk ? (flag[0][c] | (flag[1][c] << 1)) : 0;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(f != 0);
+      const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (f != 0) list[pos] = (uint16_t)(c | (f << 12));
+      count += __builtin_popcountll(m);
+    }
+    if (lane == 0) *count_slot = count;
+  }
+  __syncthreads();
+  return *count_slot;
+}
+
+// The query blocks that list key block c (from the expanded table), in
+// increasing order, into list[0 .. count); under a causal mask query blocks
+// wholly before the key block are dropped.  Every thread calls it; returns
+// count.
+template <bool CAUSAL>
+__device__ __forceinline__ int build_query_block_list(const AttnArgs& a, int c, uint16_t* list, int* count_slot) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    int count = 0;
+    for (int base = 0; base < a.n_qblk; base += 64) {
+      const int r = base + lane;
+      const bool f = r < a.n_qblk && (!CAUSAL || r >= c) && a.blk_table[(int64_t)r * a.n_kblk + c] != 0;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+      const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (f) list[pos] = (uint16_t)r;
+      count += __builtin_popcountll(m);
+    }
+    if (lane == 0) *count_slot = count;
+  }
+  __syncthreads();
+  return *count_slot;
 }
 
 }  // namespace miattn

@@ -11,6 +11,13 @@ hipError_t launch_bwd_prep_bf16(const AttnArgs& a, int d, bool varlen, hipStream
 hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 
+// mask: kMaskWindow (causal already folded into the window) or kMaskBlocks
+hipError_t launch_fwd_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dkdv_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream);
+// expands the block-sparse CSR list into a.blk_table (n_qblk x n_kblk bytes)
+hipError_t launch_block_table(const AttnArgs& a, uint8_t* table, hipStream_t stream);
+
 hipError_t launch_fwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);
 }  // namespace miattn

@@ -147,6 +147,62 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
                  int B, int H, int H_kv, int N, int d, float scale, int causal,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Forward with a sliding window, dense bf16, grouped key/value heads as in
+ * attn_fwd_gqa (H_kv == H for plain multi-head attention).  Key j is visible
+ * to query i iff i - window_left <= j <= i + window_right, a side given as -1
+ * being unbounded; with causal != 0 the right side is 0 whatever
+ * window_right says.  This is the window_size = (left, right) argument of the
+ * flash-attn interface, (-1, -1) meaning global attention ("第 18 章
+ * FlashAttention" section 18.7.1), the sliding-window pattern of section
+ * 18.8.1 (Mistral, Longformer).  Key tiles wholly outside a query tile's
+ * window are neither loaded nor computed.  A window that restricts nothing
+ * runs exactly attn_fwd_gqa.  MIATTN_ERR_INVALID_ARG also for a side < -1. */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    int window_left, int window_right, hipStream_t stream);
+
+/* Backward of attn_fwd_window; arguments as attn_bwd_gqa plus the window.
+ * workspace: attn_bwd_workspace_bytes(B,H,N,d) bytes. */
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv,
+                    int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    int window_left, int window_right,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Block-sparse layout granularity: blocks of 128 query rows x 128 keys. */
+#define MIATTN_SPARSE_BLOCK 128
+
+/* Forward with a block-sparse layout, dense bf16, grouped key/value heads as
+ * in attn_fwd_gqa.  Positions are cut into blocks of MIATTN_SPARSE_BLOCK
+ * tokens, nb = ceil(N / MIATTN_SPARSE_BLOCK) of them (N <= 131072).  The
+ * layout is a CSR list shared by every (batch, head), in device memory:
+ * row_ptr int32 [nb + 1], col_idx int32 [nnz]; query block r attends the key
+ * blocks col_idx[row_ptr[r] .. row_ptr[r+1]) ("第 18 章 FlashAttention"
+ * section 18.8.1: a per-query-block list of the key blocks to compute, built
+ * once per shape; the kernel loads only those blocks and the others add
+ * nothing to the softmax).  A block listed twice counts once; entries outside
+ * [0, nb) and positions past nnz are ignored (never read out of bounds); the
+ * order within a row does not matter.  causal != 0 also applies the causal
+ * mask.  A query row left with no key gets O = 0, LSE = -inf.
+ * MIATTN_ERR_UNSUPPORTED when N > 131072. */
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int H_kv, int N, int d, float scale, int causal,
+                          const int* row_ptr, const int* col_idx, int nnz, hipStream_t stream);
+
+/* Workspace bytes for attn_bwd_block_sparse: fp32 D (one per row) and the
+ * list expanded to an nb x nb byte table. 0 for invalid sizes. */
+size_t attn_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward of attn_fwd_block_sparse; arguments as attn_bwd_gqa plus the
+ * list.  The key-tile pass visits, for each key block, only the query blocks
+ * that list it (read from the expanded table); dk, dv of a key block no query
+ * block lists are 0. */
+int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dO, void* dq, void* dk, void* dv,
+                          int B, int H, int H_kv, int N, int d, float scale, int causal,
+                          const int* row_ptr, const int* col_idx, int nnz,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* fp32 forward: same contract as attn_fwd with fp32 q, k, v, o. */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);

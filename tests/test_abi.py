@@ -24,7 +24,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for need in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32",
-                 "attn_fwd_gqa", "attn_bwd_gqa",
+                 "attn_fwd_gqa", "attn_bwd_gqa", "attn_fwd_window", "attn_bwd_window",
+                 "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_bwd_block_sparse_workspace_bytes",
                  "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
                  "miattn_status_string"):
         assert need in names
@@ -123,3 +124,27 @@ def test_grouped_head_validation():
     assert bwd(8, 3, need) == -1
     assert bwd(8, 2, need - 4) == -1
     assert lib.attn_bwd_gqa(*([FAKE] * 8), NULL, 1, 8, 2, 64, 64, 0.125, 1, FAKE, need, NULL) == -1
+
+
+def test_window_and_block_sparse_validation():
+    lib = _lib()
+    win = lambda L, R, Hkv=2: lib.attn_fwd_window(*([FAKE] * 5), 1, 8, Hkv, 64, 64, 0.125, 0, L, R, NULL)
+    assert win(-2, 0) == -1      # a side below -1
+    assert win(4, -5) == -1
+    assert win(4, 4, Hkv=3) == -1
+    need = lib.attn_bwd_workspace_bytes(1, 8, 64, 64)
+    bwin = lambda L, R, ws: lib.attn_bwd_window(*([FAKE] * 9), 1, 8, 2, 64, 64, 0.125, 1, L, R, FAKE, ws, NULL)
+    assert bwin(-3, 0, need) == -1
+    assert bwin(16, 0, need - 4) == -1
+    sp = lambda N, rp, ci, nnz: lib.attn_fwd_block_sparse(*([FAKE] * 5), 1, 8, 2, N, 64, 0.125, 1, rp, ci, nnz, NULL)
+    assert sp(131072 + 1, FAKE, FAKE, 4) == -2     # more than 1024 blocks
+    assert sp(512, NULL, FAKE, 4) == -1            # no row pointers
+    assert sp(512, FAKE, NULL, 4) == -1            # entries but no column indices
+    assert sp(512, FAKE, FAKE, -1) == -1
+    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 131072 + 1, 64) == 0
+    nb = 4  # N = 512
+    ws = lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 512, 64)
+    assert ws >= lib.attn_bwd_workspace_bytes(1, 8, 512, 64) + nb * nb
+    bsp = lambda wsb: lib.attn_bwd_block_sparse(*([FAKE] * 9), 1, 8, 2, 512, 64, 0.125, 1, FAKE, FAKE, 4, FAKE,
+                                                wsb, NULL)
+    assert bsp(ws - 1) == -1
