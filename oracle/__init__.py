@@ -10,6 +10,8 @@ Modules
   tiled           block-by-block forward and backward in the pages' step order,
                   used only to test that tiling does not change the result
   online_softmax  the single-row running state (m, l, a) and its block ledger
+  decode          one query token per sequence against a KV cache (definition),
+                  and the pages' split-KV merge, used only to pin that rule
 
 Every function says which passage of the source pages it follows.  Pages:
   [P1] "解析 FlashAttention（4）：FlashAttention-v2" (my-webpage-adu.pages.dev)
@@ -17,4 +19,4 @@ Every function says which passage of the source pages it follows.  Pages:
   [P3] "分块 Attention：重建概率，累计梯度" (glenzli.com, attention-kernels)
   [P4] Chapter 18 "FlashAttention" of an AI-algorithms book (theaiera.top)
 """
-from . import attention, online_softmax, tiled  # noqa: F401
+from . import attention, decode, online_softmax, tiled  # noqa: F401
