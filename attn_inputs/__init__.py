@@ -22,6 +22,7 @@ __all__ = [
     "bits_to_f32",
     "dense_inputs",
     "varlen_inputs",
+    "decode_inputs",
     "left_padding_key_mask",
 ]
 
@@ -72,6 +73,18 @@ def dense_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int 
     if with_do:
         out["do"] = _draw(rng, shape, sigma_vdo, dtype)
     return out
+
+
+def decode_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
+                  sigma: float = 1.0) -> dict:
+    """One query token per sequence, q [B, H, d], and a KV cache k, v
+    [B, Hkv, N, d], drawn in that order."""
+    rng = np.random.default_rng(seed)
+    return {
+        "q": _draw(rng, (B, H, d), sigma, dtype),
+        "k": _draw(rng, (B, Hkv, N, d), sigma, dtype),
+        "v": _draw(rng, (B, Hkv, N, d), sigma, dtype),
+    }
 
 
 def varlen_inputs(nseq: int, len_lo: int, len_hi: int, H: int, d: int, dtype: str = "bf16",

@@ -54,6 +54,10 @@ WORKLOADS = {
                                                  blocks="global+local+strided16"),
 }
 SPARSE_BLOCK = 128
+# decoding: one new token per sequence against a 32768-token KV cache
+DECODE_WORKLOADS = {
+    "decode_b8_h32_hkv8_n32768_d128": dict(B=8, H=32, Hkv=8, N=32768, d=128),
+}
 
 
 def block_rows(pattern, nb):
@@ -186,12 +190,77 @@ def cpu_baseline(inp, cfg, scale, budget_s=10.0):
     }
 
 
+def run_decode(args, cfg):
+    """Decoding against a KV cache: one step is one attn_decode call (split
+    pass + merge pass) for all B sequences.  HBM-bound: value is the
+    algorithmic bytes (K and V caches once, q, O, LSE) per second."""
+    import torch
+    import exact_tiled_attention_09_amd as M
+    from attn_inputs import decode_inputs
+    B, H, Hkv, N, d = cfg["B"], cfg["H"], cfg["Hkv"], cfg["N"], cfg["d"]
+    scale = 1.0 / math.sqrt(d)
+    log(f"workload {args.workload}: generating inputs")
+    inp = decode_inputs(B, H, Hkv, N, d, "bf16", seed=0)
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda().contiguous() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.attn_decode_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in events:
+        e0.record(stream)
+        M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in events)
+    nbytes = 2 * B * Hkv * N * d * 2 + 2 * B * H * d * 2 + B * H * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": f"decode attention HBM GB/s, {args.workload}, 1 MI355X",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decoding, one token per sequence, B{B} H{H} H_kv{Hkv} KV cache N{N} d{d} bf16",
+                   "B": B, "H": H, "H_kv": Hkv, "N_kv": N, "d": d, "bytes_per_step": nbytes},
+        "decode": {"ms": round(ms, 4), "gbps": round(gbps, 1)},
+        "roofline": {"kernel": "decode_split_kernel + decode_merge_kernel (attn_decode)", "bound": "hbm",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import decode as Dc
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        Dc.decode_forward(inp["q"], inp["k"], inp["v"], scale)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+                                  "kind": "oracle", "sample": f"the whole step (all {B * H} heads) in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; its FETCH_SIZE / "
@@ -224,6 +293,8 @@ def main(argv=None):
     import exact_tiled_attention_09_amd as M
     from attn_inputs import dense_inputs
     M.load()
+    if args.workload in DECODE_WORKLOADS:
+        return run_decode(args, DECODE_WORKLOADS[args.workload])
 
     cfg = WORKLOADS[args.workload]
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]

@@ -42,6 +42,8 @@ SIGNATURES = {
     "attn_fwd_block_sparse": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _P, _P, _I, _P]),
     "attn_bwd_block_sparse_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_bwd_block_sparse": (_I, [_P] * 9 + [_I] * 5 + [_F, _I, _P, _P, _I, _P, _S, _P]),
+    "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "attn_decode": (_I, [_P] * 5 + [_I] * 5 + [_F, _P, _P, _S, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_f32": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_varlen": (_I, [_P] * 5 + [_P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
@@ -213,6 +215,25 @@ def attn_bwd_block_sparse(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal:
                                         _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)),
                                         _ptr(row_ptr), _ptr(col_idx), int(col_idx.numel()), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_workspace_bytes(B: int, H: int, H_kv: int, N_kv: int, d: int) -> int:
+    return int(load().attn_decode_workspace_bytes(B, H, H_kv, N_kv, d))
+
+
+def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_seqlens, workspace, stream=None):
+    """q, o: [B, H, d]; k_cache, v_cache: [B, H_kv, N_kv, d]; lse: [B, H];
+    cache_seqlens: int32 device tensor [B] or None."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q is [B, H, d] and the caches are [B, H_kv, N_kv, d]")
+    B, H, d = (int(x) for x in q.shape)
+    Hkv, N = int(k_cache.shape[1]), int(k_cache.shape[2])
+    if int(k_cache.shape[0]) != B or int(k_cache.shape[3]) != d:
+        raise ValueError("the caches must have the B and d of q")
+    sl = None if cache_seqlens is None else _ptr(cache_seqlens)
+    _check("attn_decode", load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, H, Hkv,
+                                             N, d, float(scale), sl, _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def attn_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

@@ -90,6 +90,35 @@ int sparse_args(AttnArgs& a, int N, const int* row_ptr, const int* col_idx, int 
   return MIATTN_OK;
 }
 
+// Split plan of decoding: about one wave per SIMD of the chip (1024 waves) in
+// total, at least 256 keys per piece, pieces a multiple of 64 keys.
+void decode_plan(int B, int H, int H_kv, int N, int* nsplit, int* chunk) {
+  const int64_t units = (int64_t)B * H_kv * ((H / H_kv + 31) / 32);
+  const int64_t want = (1024 + units - 1) / units;
+  const int64_t most = ((int64_t)N + 255) / 256;
+  int64_t ns = want < most ? want : most;
+  if (ns < 1) ns = 1;
+  int64_t ch = ((int64_t)N + ns - 1) / ns;
+  ch = (ch + 63) / 64 * 64;
+  *chunk = (int)ch;
+  *nsplit = (int)(((int64_t)N + ch - 1) / ch);
+}
+
+int check_decode(int B, int H, int H_kv, int N, int d, float scale) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || !std::isfinite(scale) || !groups_ok(H, H_kv))
+    return MIATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H_kv * N > (int64_t)1 << 40 || (int64_t)B * H > 0x7fffffffLL) return MIATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
+  return MIATTN_OK;
+}
+
+size_t decode_workspace_bytes(int B, int H, int H_kv, int N, int d) {
+  int nsplit = 0, chunk = 0;
+  decode_plan(B, H, H_kv, N, &nsplit, &chunk);
+  const size_t parts = (size_t)B * H * nsplit;
+  return round_up(parts * 2 * sizeof(float), 256) + parts * (size_t)d * sizeof(float);
+}
+
 size_t sparse_table_bytes(int N) {
   const size_t nb = ((size_t)N + miattn::kSparseBlock - 1) / miattn::kSparseBlock;
   return round_up(nb * nb, 256);
@@ -330,6 +359,40 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
   if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream)))
     return st;
   return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream));
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int N_kv, int d) {
+  if (check_decode(B, H, H_kv, N_kv, d, 1.0f) != MIATTN_OK) return 0;
+  return decode_workspace_bytes(B, H, H_kv, N_kv, d);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+                int H_kv, int N_kv, int d, float scale, const int* cache_seqlens, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k_cache) || !ptr16(v_cache) || !ptr16(o) || lse == nullptr || !aligned(lse, 4) ||
+      !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (cache_seqlens != nullptr && !aligned(cache_seqlens, 4)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_decode(B, H, H_kv, N_kv, d, scale)) return st;
+  if (workspace_bytes < decode_workspace_bytes(B, H, H_kv, N_kv, d)) return MIATTN_ERR_INVALID_ARG;
+  miattn::DecodeArgs a = {};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.seqlens = cache_seqlens;
+  a.B = B;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.N = N_kv;
+  decode_plan(B, H, H_kv, N_kv, &a.nsplit, &a.chunk);
+  const size_t parts = (size_t)B * H * a.nsplit;
+  a.part_ml = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(parts * 2 * sizeof(float), 256));
+  a.scale = scale;
+  a.scale_log2 = scale * miattn::kLog2e;
+  return hip_status(miattn::launch_decode_bf16(a, d, stream));
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,

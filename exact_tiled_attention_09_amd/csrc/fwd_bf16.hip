@@ -38,8 +38,6 @@
 
 namespace miattn {
 
-constexpr float kLazyMax = 8.0f;
-
 template <int D, int QB, int NW, int MINB, bool CAUSAL, bool VARLEN, bool KPAD>
 __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
   constexpr int BC = 64;                 // keys per tile

@@ -34,6 +34,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPosInf = __builtin_huge_valf();
+// Online softmax with a lazy reference max: a row's reference is raised only
+// when a tile's max exceeds it by more than this (base-2 units), so P~ stays
+// below 2^kLazyMax; any reference gives the same O and LSE up to rounding.
+constexpr float kLazyMax = 8.0f;
 
 // Everything a kernel needs to address one problem.  Dense tensors are
 // [B, H, N, d] with LSE/D as [B, H, N]; packed tensors are [T, H, d] with
@@ -75,6 +79,30 @@ struct AttnArgs {
   int n_qblk;
   int n_kblk;
   const uint8_t* blk_table;
+};
+
+// Decoding against a KV cache (one query token per sequence), split along
+// the cache: q, o [B, H, D]; k, v [B, Hkv, N, D]; lse [B, H]; piece t of a
+// sequence covers keys [t * chunk, (t + 1) * chunk).  part_ml [B*H][nsplit][2]
+// holds each piece's (max in base-2 units, sum), part_o [B*H][nsplit][D] its
+// unnormalised output.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* seqlens;  // [B] cache lengths, or null for N
+  float* part_o;
+  float* part_ml;
+  int B;
+  int H;
+  int Hkv;
+  int N;
+  int nsplit;
+  int chunk;
+  float scale;
+  float scale_log2;
 };
 
 // Mask modes of the kernels besides none / causal.

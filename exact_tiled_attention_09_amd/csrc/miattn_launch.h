@@ -4,6 +4,7 @@
 
 namespace miattn {
 struct AttnArgs;
+struct DecodeArgs;
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 hipError_t launch_fwd_w4_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
@@ -17,6 +18,9 @@ hipError_t launch_bwd_dkdv_masked_bf16(const AttnArgs& a, int d, int mask, bool 
 hipError_t launch_bwd_dq_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream);
 // expands the block-sparse CSR list into a.blk_table (n_qblk x n_kblk bytes)
 hipError_t launch_block_table(const AttnArgs& a, uint8_t* table, hipStream_t stream);
+
+// split pass then merge pass of decoding against a KV cache
+hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);

@@ -203,6 +203,26 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
                           const int* row_ptr, const int* col_idx, int nnz,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes for attn_decode (the pieces' running states); 0 for
+ * invalid sizes. */
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int N_kv, int d);
+
+/* Decoding attention, bf16: one new query token per sequence against a KV
+ * cache ("第 18 章 FlashAttention" section 18.8.2, the decoding phase with
+ * Q: [b, 1, d], and FlashDecoding).  q, o: [B,H,d]; k_cache, v_cache:
+ * [B,H_kv,N_kv,d]; lse: [B,H] fp32.  Query head h of sequence b attends keys
+ * 0 .. len_b - 1 of key/value head h / (H / H_kv), with len_b =
+ * cache_seqlens[b] (device int32 [B], clamped to [0, N_kv]) or N_kv when
+ * cache_seqlens is NULL; no other mask (the cached positions all precede the
+ * new token, whose own K/V the caller has appended).  The cache is cut into
+ * pieces processed in parallel, each keeping its own running max, sum and
+ * unnormalised output, merged at the end with the online-softmax rule
+ * (section 18.8.2, step 3).  A sequence with len_b = 0 gets O = 0, LSE = -inf.
+ * workspace: attn_decode_workspace_bytes(B,H,H_kv,N_kv,d) bytes. */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                int B, int H, int H_kv, int N_kv, int d, float scale, const int* cache_seqlens,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* fp32 forward: same contract as attn_fwd with fp32 q, k, v, o. */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);

@@ -26,6 +26,7 @@ def test_header_declares_the_entry_points():
     for need in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32",
                  "attn_fwd_gqa", "attn_bwd_gqa", "attn_fwd_window", "attn_bwd_window",
                  "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_bwd_block_sparse_workspace_bytes",
+                 "attn_decode", "attn_decode_workspace_bytes",
                  "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
                  "miattn_status_string"):
         assert need in names
@@ -148,3 +149,16 @@ def test_window_and_block_sparse_validation():
     bsp = lambda wsb: lib.attn_bwd_block_sparse(*([FAKE] * 9), 1, 8, 2, 512, 64, 0.125, 1, FAKE, FAKE, 4, FAKE,
                                                 wsb, NULL)
     assert bsp(ws - 1) == -1
+
+
+def test_decode_validation():
+    lib = _lib()
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 1000, 128)
+    assert need > 0
+    assert lib.attn_decode_workspace_bytes(2, 8, 3, 1000, 128) == 0   # 3 does not divide 8
+    assert lib.attn_decode_workspace_bytes(2, 8, 2, 0, 128) == 0      # empty cache dimension
+    dec = lambda H, Hkv, N, d, ws, sl=NULL: lib.attn_decode(*([FAKE] * 5), 2, H, Hkv, N, d, 0.1, sl, FAKE, ws, NULL)
+    assert dec(8, 2, 1000, 128, need - 1) == -1
+    assert dec(8, 3, 1000, 128, need) == -1
+    assert dec(8, 2, 1000, 96, need) == -2
+    assert dec(8, 2, 1000, 128, need, ctypes.c_void_p((1 << 20) + 2)) == -1   # misaligned lengths
