@@ -12,6 +12,9 @@ Modules
   online_softmax  the single-row running state (m, l, a) and its block ledger
   decode          one query token per sequence against a KV cache (definition),
                   and the pages' split-KV merge, used only to pin that rule
+  fp8             E4M3 encoding, per-block quantization, the FP8 attention
+                  reference (exact attention on dequantized inputs) and its
+                  error bound
 
 Every function says which passage of the source pages it follows.  Pages:
   [P1] "解析 FlashAttention（4）：FlashAttention-v2" (my-webpage-adu.pages.dev)
@@ -19,4 +22,4 @@ Every function says which passage of the source pages it follows.  Pages:
   [P3] "分块 Attention：重建概率，累计梯度" (glenzli.com, attention-kernels)
   [P4] Chapter 18 "FlashAttention" of an AI-algorithms book (theaiera.top)
 """
-from . import attention, decode, online_softmax, tiled  # noqa: F401
+from . import attention, decode, fp8, online_softmax, tiled  # noqa: F401
