@@ -54,6 +54,11 @@ WORKLOADS = {
                                                  blocks="global+local+strided16"),
 }
 SPARSE_BLOCK = 128
+# FP8 (E4M3) forward: quantize Q, K, V from bf16, then the FP8 forward
+FP8_WORKLOADS = {
+    "fp8_causal_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128, causal=True),
+}
+PEAK_FP8_TFLOPS = 5033.2    # 2 x the bf16 dense peak
 # decoding: one new token per sequence against a 32768-token KV cache
 DECODE_WORKLOADS = {
     "decode_b8_h32_hkv8_n32768_d128": dict(B=8, H=32, Hkv=8, N=32768, d=128),
@@ -190,6 +195,83 @@ def cpu_baseline(inp, cfg, scale, budget_s=10.0):
     }
 
 
+def run_fp8(args, cfg):
+    """FP8 forward: one step quantizes Q, K, V (bf16 -> E4M3 codes + scales)
+    and runs the FP8 forward.  value: forward FLOPs / whole step time; the
+    roofline is the FP8 forward kernel alone against the FP8 dense peak."""
+    import torch
+    import exact_tiled_attention_09_amd as M
+    from attn_inputs import dense_inputs
+    B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
+    scale = 1.0 / math.sqrt(d)
+    log(f"workload {args.workload}: generating inputs")
+    inp = dense_inputs(B, H, N, d, "bf16", seed=0, with_do=False)
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda().contiguous() for n in ("q", "k", "v"))
+    nb = (N + 63) // 64
+    q8, k8 = (torch.empty((B, H, N, d), dtype=torch.uint8, device="cuda") for _ in range(2))
+    v8 = torch.empty((B, H, nb, d, 64), dtype=torch.uint8, device="cuda")
+    sq, sk = (torch.empty((B, H, nb), dtype=torch.float32, device="cuda") for _ in range(2))
+    sv = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.attn_quantize_fp8_rows(q, q8, sq, stream)
+        M.attn_quantize_fp8_rows(k, k8, sk, stream)
+        M.attn_quantize_fp8_vt(v, v8, sv, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.attn_fwd_fp8(q8, sq, k8, sk, v8, sv, o, lse, scale, causal, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
+    f_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
+    f_fwd, _ = flops(B, H, N, d, causal)
+    ms_step = wall * 1e3 / args.steps
+    fwd_tf = f_fwd / (f_ms * 1e-3) / 1e12
+    qbytes = 3 * B * H * N * d * 2 + 3 * B * H * N * d + B * H * (2 * nb + 1) * 4
+    result = {
+        "metric": f"attn fp8 fwd TFLOPS, {args.workload}, 1 MI355X",
+        "value": round(f_fwd / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"exact attention FP8 E4M3 forward (with quantization), "
+                               f"{'causal' if causal else 'non-causal'} B{B} H{H} N{N} d{d}",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "flops_fwd": f_fwd},
+        "quantize": {"ms": round(q_ms, 4), "gbps": round(qbytes / (q_ms * 1e-3) / 1e9, 1)},
+        "fwd": {"ms": round(f_ms, 4), "tflops": round(fwd_tf, 2),
+                "pct_fp8_peak": round(100 * fwd_tf / PEAK_FP8_TFLOPS, 2),
+                "pct_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"kernel": "fwd_fp8_kernel (attn_fwd_fp8)", "bound": "mfma", "achieved": round(fwd_tf, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": f_fwd, "avg_launch_ms": round(f_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def run_decode(args, cfg):
     """Decoding against a KV cache: one step is one attn_decode call (split
     pass + merge pass) for all B sequences.  HBM-bound: value is the
@@ -260,7 +342,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT,
+                    choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS) + sorted(FP8_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; its FETCH_SIZE / "
@@ -295,6 +378,8 @@ def main(argv=None):
     M.load()
     if args.workload in DECODE_WORKLOADS:
         return run_decode(args, DECODE_WORKLOADS[args.workload])
+    if args.workload in FP8_WORKLOADS:
+        return run_fp8(args, FP8_WORKLOADS[args.workload])
 
     cfg = WORKLOADS[args.workload]
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]

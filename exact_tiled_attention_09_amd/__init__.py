@@ -10,6 +10,7 @@ script.  Functions carry the C names and take device tensors:
     attn_fwd_window, attn_bwd_window,
     attn_fwd_block_sparse, attn_bwd_block_sparse, attn_bwd_block_sparse_workspace_bytes,
     attn_decode, attn_decode_workspace_bytes,
+    attn_quantize_fp8_rows, attn_quantize_fp8_vt, attn_fwd_fp8,
     attn_fwd_f32, attn_bwd_f32, attn_bwd_f32_workspace_bytes,
     attn_fwd_varlen, attn_bwd_varlen, attn_bwd_varlen_workspace_bytes
 """
@@ -33,10 +34,13 @@ from ._lib import (  # noqa: F401
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_f32,
+    attn_fwd_fp8,
     attn_fwd_block_sparse,
     attn_fwd_gqa,
     attn_fwd_window,
     attn_fwd_varlen,
+    attn_quantize_fp8_rows,
+    attn_quantize_fp8_vt,
     load,
     miattn_status_string,
     miattn_version,

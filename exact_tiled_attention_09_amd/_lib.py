@@ -44,6 +44,9 @@ SIGNATURES = {
     "attn_bwd_block_sparse": (_I, [_P] * 9 + [_I] * 5 + [_F, _I, _P, _P, _I, _P, _S, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P] * 5 + [_I] * 5 + [_F, _P, _P, _S, _P]),
+    "attn_quantize_fp8_rows": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_quantize_fp8_vt": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_fwd_fp8": (_I, [_P] * 8 + [_I] * 5 + [_F, _I, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_f32": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_varlen": (_I, [_P] * 5 + [_P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
@@ -234,6 +237,28 @@ def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_seqlens, worksp
     _check("attn_decode", load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, H, Hkv,
                                              N, d, float(scale), sl, _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_quantize_fp8_rows(x, x8, scales, stream=None):
+    """x bf16 [B, H, N, d] -> x8 uint8 [B, H, N, d], scales fp32 [B, H, ceil(N/64)]."""
+    B, H, N, d = _dense_dims(x)
+    _check("attn_quantize_fp8_rows", load().attn_quantize_fp8_rows(_ptr(x), _ptr(x8), _ptr(scales), B, H, N, d,
+                                                                   _stream(stream)))
+
+
+def attn_quantize_fp8_vt(v, v8t, scales, stream=None):
+    """v bf16 [B, H, N, d] -> v8t uint8 [B, H, ceil(N/64), d, 64], scales fp32 [B, H]."""
+    B, H, N, d = _dense_dims(v)
+    _check("attn_quantize_fp8_vt", load().attn_quantize_fp8_vt(_ptr(v), _ptr(v8t), _ptr(scales), B, H, N, d,
+                                                               _stream(stream)))
+
+
+def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, o, lse, scale: float, causal: bool, stream=None):
+    B, H, N, d = _dense_dims(q8)
+    Hkv = int(k8.shape[1])
+    _check("attn_fwd_fp8", load().attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8t),
+                                               _ptr(v_scale), _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale),
+                                               int(bool(causal)), _stream(stream)))
 
 
 def attn_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

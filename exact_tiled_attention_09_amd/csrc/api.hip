@@ -406,6 +406,49 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
   return hip_status(miattn::launch_decode_bf16(a, d, stream));
 }
 
+int attn_quantize_fp8_rows(const void* x, unsigned char* x8, float* scales, int B, int H, int N, int d,
+                           hipStream_t stream) {
+  if (!ptr16(x) || !ptr16(x8) || scales == nullptr || !aligned(scales, 4)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, 1.0f)) return st;
+  if (d != 128) return MIATTN_ERR_UNSUPPORTED;
+  return hip_status(miattn::launch_quant_rows_fp8(x, x8, scales, B * H, N, d, stream));
+}
+
+int attn_quantize_fp8_vt(const void* v, unsigned char* v8t, float* scales, int B, int H, int N, int d,
+                         hipStream_t stream) {
+  if (!ptr16(v) || !ptr16(v8t) || scales == nullptr || !aligned(scales, 4)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, 1.0f)) return st;
+  if (d != 128) return MIATTN_ERR_UNSUPPORTED;
+  return hip_status(miattn::launch_quant_vt_fp8(v, v8t, scales, B * H, N, d, stream));
+}
+
+int attn_fwd_fp8(const unsigned char* q8, const float* q_scale, const unsigned char* k8, const float* k_scale,
+                 const unsigned char* v8t, const float* v_scale, void* o, float* lse, int B, int H, int H_kv, int N,
+                 int d, float scale, int causal, hipStream_t stream) {
+  if (!ptr16(q8) || !ptr16(k8) || !ptr16(v8t) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;
+  for (const float* p : {q_scale, k_scale, v_scale})
+    if (p == nullptr || !aligned(p, 4)) return MIATTN_ERR_INVALID_ARG;
+  if (!groups_ok(H, H_kv)) return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  if (d != 128) return MIATTN_ERR_UNSUPPORTED;
+  miattn::Fp8Args a = {};
+  a.q8 = q8;
+  a.q_scale = q_scale;
+  a.k8 = k8;
+  a.k_scale = k_scale;
+  a.v8t = v8t;
+  a.v_scale = v_scale;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.N = N;
+  a.scale = scale;
+  a.scale_log2 = scale * miattn::kLog2e;
+  return hip_status(miattn::launch_fwd_fp8(a, d, causal != 0, stream));
+}
+
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
                  float scale, int causal, hipStream_t stream) {
   if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse)) return MIATTN_ERR_INVALID_ARG;

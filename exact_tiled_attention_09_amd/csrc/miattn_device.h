@@ -105,6 +105,27 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+// FP8 (E4M3) forward: codes and their fp32 scales.  Q [B, H, N, D] and K
+// [B, Hkv, N, D] codes with one scale per 64-row block ([.., ceil(N/64)]);
+// V codes per 64-key tile transposed, [B, Hkv, ceil(N/64), D, 64], one scale
+// per (batch, head).
+struct Fp8Args {
+  const uint8_t* q8;
+  const float* q_scale;
+  const uint8_t* k8;
+  const float* k_scale;
+  const uint8_t* v8t;
+  const float* v_scale;
+  void* o;
+  float* lse;
+  int B;
+  int H;
+  int Hkv;
+  int N;
+  float scale;
+  float scale_log2;
+};
+
 // Mask modes of the kernels besides none / causal.
 enum : int { kMaskPlain = 0, kMaskWindow = 1, kMaskBlocks = 2 };
 constexpr int kSparseBlock = 128;       // tokens per block of a block-sparse list

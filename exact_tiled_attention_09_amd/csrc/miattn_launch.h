@@ -5,6 +5,7 @@
 namespace miattn {
 struct AttnArgs;
 struct DecodeArgs;
+struct Fp8Args;
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 hipError_t launch_fwd_w4_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
@@ -21,6 +22,11 @@ hipError_t launch_block_table(const AttnArgs& a, uint8_t* table, hipStream_t str
 
 // split pass then merge pass of decoding against a KV cache
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t stream);
+
+// FP8: quantizers (bf16 -> E4M3 codes + scales) and the forward, D = 128
+hipError_t launch_quant_rows_fp8(const void* x, void* x8, float* scales, int BH, int N, int d, hipStream_t stream);
+hipError_t launch_quant_vt_fp8(const void* v, void* v8t, float* scales, int BH, int N, int d, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Args& a, int d, bool causal, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnArgs& a, int d, bool causal, hipStream_t stream);

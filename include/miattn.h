@@ -223,6 +223,38 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 int B, int H, int H_kv, int N_kv, int d, float scale, const int* cache_seqlens,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* FP8 (E4M3) attention ("第 18 章 FlashAttention" section 18.6.2: Q, K, V
+ * converted to FP8 E4M3 with dynamic per-block scales s = max|X_block| / 448
+ * for the load blocks of Q and K; S = QK^T and the softmax in fp32; O
+ * dequantized).  Head dimension 128 only (MIATTN_ERR_UNSUPPORTED otherwise).
+ * Codes are OCP E4M3FN (bias 7, largest magnitude 448), rounded to nearest
+ * even; an all-zero block gets scale 1.
+ *
+ * attn_quantize_fp8_rows: x bf16 [B,H,N,128] -> x8 codes [B,H,N,128] and
+ * scales fp32 [B,H,ceil(N/64)], one per block of 64 rows (for Q and for K).
+ *
+ * attn_quantize_fp8_vt: v bf16 [B,H,N,128] -> scales fp32 [B,H] (one per
+ * head) and v8t codes [B,H,ceil(N/64),128,64]: tile t, feature f, position p
+ * holds key 64t + k(p), k(p) = 32 (p%32/16) + 8 (p%16/4) + 4 (p/32) + p%4,
+ * keys past N coded 0 (the order in which the forward's score accumulators
+ * hold a tile's keys).  Queues four small kernels; scales is overwritten. */
+int attn_quantize_fp8_rows(const void* x, unsigned char* x8, float* scales, int B, int H, int N, int d,
+                           hipStream_t stream);
+int attn_quantize_fp8_vt(const void* v, unsigned char* v8t, float* scales, int B, int H, int N, int d,
+                         hipStream_t stream);
+
+/* FP8 forward, grouped key/value heads as attn_fwd_gqa: q8, q_scale from
+ * attn_quantize_fp8_rows of Q [B,H,N,128]; k8, k_scale of K [B,H_kv,N,128];
+ * v8t, v_scale from attn_quantize_fp8_vt of V [B,H_kv,N,128].  o bf16
+ * [B,H,N,128], lse fp32 [B,H,N].  The P V product uses P rounded to E4M3
+ * (after a power-of-two scaling that keeps every P >= 2^-12 a normal E4M3
+ * value), so O differs from exact attention on the dequantized inputs by at
+ * most about 2^-4 sum_j P_ij |V_j| per element; LSE is that of the fp32
+ * scores.  Fully masked rows and errors as attn_fwd. */
+int attn_fwd_fp8(const unsigned char* q8, const float* q_scale, const unsigned char* k8, const float* k_scale,
+                 const unsigned char* v8t, const float* v_scale, void* o, float* lse,
+                 int B, int H, int H_kv, int N, int d, float scale, int causal, hipStream_t stream);
+
 /* fp32 forward: same contract as attn_fwd with fp32 q, k, v, o. */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);

@@ -20,8 +20,9 @@ Readings (each listed in the design doc):
     all-zero block gets s = 1.
   * The reference output is exact attention (this package's definition) on
     the dequantized tensors s * E4M3value; what the FP8 path adds on top (the
-    rounding of P to E4M3 for the P V product, fp32 accumulation) is bounded
-    in ``fp8_output_bound``.
+    rounding of P, scaled by a power of two, to E4M3 for the P V product) is
+    bounded in ``fp8_output_bound``, including P small enough to be an E4M3
+    subnormal after the scaling.
 """
 from __future__ import annotations
 
@@ -156,18 +157,26 @@ def fp8_reference(q, k, v, scale, causal=False):
             "qd": qd, "kd": kd, "vd": vd}
 
 
-def fp8_output_bound(qd, kd, vd, lse, scale, causal=False):
+def fp8_output_bound(qd, kd, vd, lse, scale, causal=False, p_scale_log2=6):
     """Per-element bound on |O_fp8 - O_ref| from rounding P to E4M3 for the
-    P V product: each P_ij is off by at most 2^-4 of itself (half an ulp of a
-    3-bit mantissa, P kept in the normal range), so the error of O_i is at
-    most 2^-4 sum_j P_ij |V_j|.  Returns that bound [B, H, N, d] (fp64)."""
+    P V product, P being multiplied by 2^p_scale_log2 before rounding.  A P_ij
+    whose scaled value is a normal E4M3 number is off by at most 2^-4 of
+    itself (half an ulp of a 3-bit mantissa); below that (subnormal) it is off
+    by at most half the subnormal step, 2^-10 / 2^p_scale_log2, and never by
+    more than itself.  The error of O_i is at most
+    sum_j min(P_ij, max(2^-4 P_ij, 2^-10 / 2^p_scale_log2)) |V_j|.
+    Returns (bound, weighted) [B, H, N, d] fp64, weighted = sum_j P_ij |V_j|."""
     B, H, N, d = qd.shape
     G = H // kd.shape[1]
-    out = np.zeros(qd.shape)
+    floor_ = 2.0 ** -10 / 2.0 ** p_scale_log2
+    bound = np.zeros(qd.shape)
+    weighted = np.zeros(qd.shape)
     for b in range(B):
         for h in range(H):
             s = scale * (qd[b, h] @ kd[b, h // G].T)
             s = np.where(visible_mask(np.arange(N), N, causal), s, -np.inf)
             p = np.exp(s - lse[b, h][:, None])
-            out[b, h] = 2.0 ** -4 * (p @ np.abs(vd[b, h // G]))
-    return out
+            dp = np.minimum(p, np.maximum(2.0 ** -4 * p, floor_))
+            bound[b, h] = dp @ np.abs(vd[b, h // G])
+            weighted[b, h] = p @ np.abs(vd[b, h // G])
+    return bound, weighted

@@ -27,6 +27,7 @@ def test_header_declares_the_entry_points():
                  "attn_fwd_gqa", "attn_bwd_gqa", "attn_fwd_window", "attn_bwd_window",
                  "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_bwd_block_sparse_workspace_bytes",
                  "attn_decode", "attn_decode_workspace_bytes",
+                 "attn_quantize_fp8_rows", "attn_quantize_fp8_vt", "attn_fwd_fp8",
                  "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
                  "miattn_status_string"):
         assert need in names
@@ -162,3 +163,13 @@ def test_decode_validation():
     assert dec(8, 3, 1000, 128, need) == -1
     assert dec(8, 2, 1000, 96, need) == -2
     assert dec(8, 2, 1000, 128, need, ctypes.c_void_p((1 << 20) + 2)) == -1   # misaligned lengths
+
+
+def test_fp8_validation():
+    lib = _lib()
+    assert lib.attn_quantize_fp8_rows(FAKE, FAKE, FAKE, 1, 2, 64, 64, NULL) == -2     # head dim 64
+    assert lib.attn_quantize_fp8_vt(FAKE, FAKE, NULL, 1, 2, 64, 128, NULL) == -1      # no scales
+    fwd = lambda Hkv, d: lib.attn_fwd_fp8(*([FAKE] * 8), 1, 8, Hkv, 64, d, 0.1, 1, NULL)
+    assert fwd(3, 128) == -1
+    assert fwd(2, 64) == -2
+    assert lib.attn_fwd_fp8(FAKE, NULL, *([FAKE] * 6), 1, 8, 2, 64, 128, 0.1, 1, NULL) == -1

@@ -138,15 +138,22 @@ def test_bound_covers_rounding_p_to_e4m3():
     than fp8_output_bound."""
     rng = np.random.default_rng(4)
     q, k, v = (rng.standard_normal((1, 2, 96, 16)).astype(np.float32) for _ in range(3))
-    ref = F.fp8_reference(q, k, v, 0.25, causal=True)
-    bound = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], 0.25, causal=True)
-    for h in range(2):
-        s = 0.25 * ref["qd"][0, h] @ ref["kd"][0, h].T
-        s = np.where(np.tril(np.ones((96, 96), bool)), s, -np.inf)
-        p = np.exp(s - ref["lse"][0, h][:, None])
-        pq = V[F.e4m3_encode((p * 64).astype(np.float32))] / 64
-        o_sim = pq @ ref["vd"][0, h]
-        assert np.all(np.abs(o_sim - ref["o"][0, h]) <= bound[0, h] + 1e-12)
+    for sig, sc in ((1.0, 0.25), (3.0, 0.9)):   # the second has many P below 2^-12 (subnormal after x 2^6)
+        q, k, v = (rng.standard_normal((1, 2, 96, 16)).astype(np.float32) * sig for _ in range(3))
+        ref = F.fp8_reference(q, k, v, sc, causal=True)
+        bound, weighted = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], sc, causal=True)
+        assert np.all(bound <= 2.0 ** -4 * weighted + 1e-300 + 2.0 ** -16 * np.abs(ref["vd"]).sum(axis=2)[:, :, None])
+        tight = 0.0
+        for h in range(2):
+            s = sc * ref["qd"][0, h] @ ref["kd"][0, h].T
+            s = np.where(np.tril(np.ones((96, 96), bool)), s, -np.inf)
+            p = np.exp(s - ref["lse"][0, h][:, None])
+            pq = V[F.e4m3_encode((p * 64).astype(np.float32))] / 64
+            o_sim = pq @ ref["vd"][0, h]
+            err = np.abs(o_sim - ref["o"][0, h])
+            assert np.all(err <= bound[0, h] * (1 + 1e-9) + 1e-15)
+            tight = max(tight, float(np.max(err / np.maximum(bound[0, h], 1e-300))))
+        assert tight > 0.2   # the bound is not vacuous
 
 
 def _mutant(old, new):
