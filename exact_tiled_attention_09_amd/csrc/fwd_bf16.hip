@@ -1040,7 +1040,8 @@ static hipError_t dispatch_fwd(const AttnArgs& a, bool causal, bool varlen, bool
 //   4 the four-wave form with 64 rows per wave (fwd_w4.hip);
 //   5 the direct-load form with four waves and two buffers (two
 //     workgroups per CU);
-//   6 the direct-load form with four buffers (loads three tiles ahead).
+//   6 the direct-load form with four buffers (loads three tiles ahead);
+//   7 split roles per SIMD (fwd_split.hip, dense layout only).
 static int fwd_tile_choice() {
   static int choice = [] {
     const char* e = getenv("MIATTN_FWD_TILE");
@@ -1053,6 +1054,7 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, h
   const bool kpad = varlen && a.key_valid != nullptr;
   const int t = fwd_tile_choice();
   if (t == 4) return launch_fwd_w4_bf16(a, d, causal, varlen, stream);
+  if (t == 7 && !varlen) return launch_fwd_split_bf16(a, d, causal, stream);
   if (d == 128) {
     if (t == 1) return dispatch_fwd_dma<128, 8, 3>(a, causal, varlen, kpad, stream);
     if (t == 2) return dispatch_fwd_stag<128, 1>(a, causal, varlen, kpad, stream);
