@@ -396,8 +396,8 @@ def main(argv=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_bytes = M.attn_bwd_workspace_bytes(B, H, N, d)
     if "blocks" in cfg:
-        ws_bytes = M.attn_bwd_block_sparse_workspace_bytes(B, H, N, d)
         mk = oracle_mask(cfg)["blocks"]
+        ws_bytes = M.attn_bwd_block_sparse_workspace_bytes(B, H, Hkv, N, d, len(mk[1]))
         row_ptr = torch.from_numpy(mk[0]).cuda()
         col_idx = torch.from_numpy(mk[1]).cuda()
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

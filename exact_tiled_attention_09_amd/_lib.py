@@ -40,7 +40,7 @@ SIGNATURES = {
     "attn_fwd_window": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _I, _I, _P]),
     "attn_bwd_window": (_I, [_P] * 9 + [_I] * 5 + [_F, _I, _I, _I, _P, _S, _P]),
     "attn_fwd_block_sparse": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _P, _P, _I, _P]),
-    "attn_bwd_block_sparse_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_bwd_block_sparse_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_bwd_block_sparse": (_I, [_P] * 9 + [_I] * 5 + [_F, _I, _P, _P, _I, _P, _S, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P] * 5 + [_I] * 5 + [_F, _P, _P, _S, _P]),
@@ -206,8 +206,8 @@ def attn_fwd_block_sparse(q, k, v, o, lse, scale: float, causal: bool, row_ptr, 
                                         int(col_idx.numel()), _stream(stream)))
 
 
-def attn_bwd_block_sparse_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    return int(load().attn_bwd_block_sparse_workspace_bytes(B, H, N, d))
+def attn_bwd_block_sparse_workspace_bytes(B: int, H: int, H_kv: int, N: int, d: int, nnz: int) -> int:
+    return int(load().attn_bwd_block_sparse_workspace_bytes(B, H, H_kv, N, d, nnz))
 
 
 def attn_bwd_block_sparse(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, row_ptr, col_idx,

@@ -135,6 +135,34 @@ size_t sparse_table_bytes(int N) {
   return round_up(nb * nb, 256);
 }
 
+// Balanced key-tile pass over a block list: a key block listed by more than
+// `chunk` query blocks is cut into chunks of `chunk` (the average list
+// length, at least 4).  A cut block with list length n > chunk takes
+// ceil(n / chunk) < 2 n / chunk chunks, and the list lengths add up to at
+// most nnz, so fewer than 2 nnz / chunk partial slots and at most
+// nb + nnz / chunk work items exist.
+struct SparsePlan {
+  int nb, chunk, max_work, max_slots;
+  size_t off_table, off_work, off_slot, off_nch, off_part, total;
+};
+
+SparsePlan sparse_plan(int B, int H, int H_kv, int N, int d, int nnz) {
+  SparsePlan p;
+  p.nb = (N + miattn::kSparseBlock - 1) / miattn::kSparseBlock;
+  const int avg = (nnz + p.nb - 1) / p.nb;
+  p.chunk = avg > 4 ? avg : 4;
+  p.max_work = p.nb + (nnz + p.chunk - 1) / p.chunk;
+  p.max_slots = (2 * nnz + p.chunk - 1) / p.chunk + 1;
+  const int64_t rows = (int64_t)B * H * N;
+  p.off_table = workspace_bytes_for(rows);
+  p.off_work = p.off_table + sparse_table_bytes(N);
+  p.off_slot = p.off_work + round_up((size_t)(1 + p.max_work) * sizeof(int), 256);
+  p.off_nch = p.off_slot + round_up((size_t)p.nb * sizeof(int), 256);
+  p.off_part = p.off_nch + round_up((size_t)p.nb * sizeof(int), 256);
+  p.total = p.off_part + (size_t)B * H_kv * p.max_slots * 2 * miattn::kSparseBlock * d * sizeof(float);
+  return p;
+}
+
 AttnArgs dense_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
                     int N, float scale) {
   AttnArgs a = {};
@@ -338,10 +366,10 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
   return hip_status(miattn::launch_fwd_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream));
 }
 
-size_t attn_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d) {
-  if (check_dense(B, H, N, d, 1.0f) != MIATTN_OK) return 0;
+size_t attn_bwd_block_sparse_workspace_bytes(int B, int H, int H_kv, int N, int d, int nnz) {
+  if (check_dense(B, H, N, d, 1.0f) != MIATTN_OK || !groups_ok(H, H_kv) || nnz < 0) return 0;
   if (N > miattn::kMaxSparseBlocks * miattn::kSparseBlock) return 0;
-  return workspace_bytes_for((int64_t)B * H * N) + sparse_table_bytes(N);
+  return sparse_plan(B, H, H_kv, N, d, nnz).total;
 }
 
 int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -356,20 +384,34 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
   const int64_t rows = (int64_t)B * H * N;
   AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
   if (int st = sparse_args(a, N, row_ptr, col_idx, nnz)) return st;
-  if (workspace_bytes < workspace_bytes_for(rows) + sparse_table_bytes(N)) return MIATTN_ERR_INVALID_ARG;
+  const SparsePlan plan = sparse_plan(B, H, H_kv, N, d, nnz);
+  if (workspace_bytes < plan.total) return MIATTN_ERR_INVALID_ARG;
   a.Hkv = H_kv;
   a.dout = dO;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
   carve(a, workspace, rows);
-  uint8_t* table = static_cast<uint8_t*>(workspace) + workspace_bytes_for(rows);
+  char* ws = static_cast<char*>(workspace);
+  uint8_t* table = reinterpret_cast<uint8_t*>(ws + plan.off_table);
+  int* work = reinterpret_cast<int*>(ws + plan.off_work);
+  int* slot = reinterpret_cast<int*>(ws + plan.off_slot);
+  int* nch = reinterpret_cast<int*>(ws + plan.off_nch);
   a.blk_table = table;
+  a.blk_work = work;
+  a.blk_slot = slot;
+  a.blk_nch = nch;
+  a.blk_part = reinterpret_cast<float*>(ws + plan.off_part);
+  a.blk_chunk = plan.chunk;
+  a.blk_nslots = plan.max_slots;
+  a.blk_max_work = plan.max_work;
+  const bool c = causal != 0;
   if (int st = hip_status(miattn::launch_block_table(a, table, stream))) return st;
+  if (int st = hip_status(miattn::launch_block_work(a, c, work, slot, nch, stream))) return st;
   if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream)))
-    return st;
-  return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, miattn::kMaskBlocks, causal != 0, stream));
+  if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, miattn::kMaskBlocks, c, stream))) return st;
+  if (int st = hip_status(miattn::launch_block_reduce(a, d, stream))) return st;
+  return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, miattn::kMaskBlocks, c, stream));
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int N_kv, int d) {

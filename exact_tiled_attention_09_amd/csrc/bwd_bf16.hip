@@ -107,7 +107,18 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   // that read this key/value head, so dK and dV sum over the group in
   // registers.
   int bh, kt;
-  wg_coords(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
+  int chunk = 0;  // block list: which chunk of the key block's query list
+  if constexpr (MASK == kMaskBlocks) {
+    // one work item (key block, chunk) of the balanced list per workgroup
+    bh = blockIdx.x / a.blk_max_work;
+    const int wi = blockIdx.x - bh * a.blk_max_work;
+    if (wi >= a.blk_work[0]) return;  // uniform, before any barrier
+    const int item = a.blk_work[1 + wi];
+    kt = item & 0xffff;
+    chunk = item >> 16;
+  } else {
+    wg_coords(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
+  }
   const int G = a.H / a.Hkv;
   const int b = bh / a.Hkv;
   const int hk = bh - b * a.Hkv;
@@ -154,7 +165,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   const int n_qt = (len + BQ - 1) / BQ;
   __shared__ uint16_t s_qlist[MASK == kMaskBlocks ? kMaxSparseBlocks : 1];
   __shared__ int s_qcount;
-  int qt_begin = 0, nsteps;
+  int qt_begin = 0, nsteps, seg0 = 0;
   if constexpr (MASK == kMaskPlain) {
     qt_begin = CAUSAL ? k0 / BQ : 0;
     nsteps = n_qt - qt_begin;
@@ -163,10 +174,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     nsteps = min(n_qt - 1, (k0 + BK - 1 + a.win_left) / BQ) - qt_begin + 1;
   } else {
     static_assert(BK == kSparseBlock && 2 * BQ == kSparseBlock, "one key block per workgroup");
-    nsteps = 2 * build_query_block_list<CAUSAL>(a, kt, s_qlist, &s_qcount);
+    const int count = build_query_block_list<CAUSAL>(a, kt, s_qlist, &s_qcount);
+    seg0 = chunk * a.blk_chunk;  // this workgroup's part of the list
+    nsteps = 2 * max(0, min(count - seg0, a.blk_chunk));
   }
   auto tile_at = [&](int p) __attribute__((always_inline)) -> int {
-    if constexpr (MASK == kMaskBlocks) return 2 * (int)s_qlist[p >> 1] + (p & 1);
+    if constexpr (MASK == kMaskBlocks) return 2 * (int)s_qlist[seg0 + (p >> 1)] + (p & 1);
     else return qt_begin + p;
   };
   // Steps v = 0 .. nv-1 run list position v % nsteps of the group's query
@@ -424,6 +437,25 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
         dk[db][r] += red[(((kblk * 2 + 0) * DB + db) * 16 + r) * 64 + lane];
         dv[db][r] += red[(((kblk * 2 + 1) * DB + db) * 16 + r) * 64 + lane];
       }
+  }
+
+  if constexpr (MASK == kMaskBlocks) {
+    // A key block cut into chunks: this chunk's fp32 sums go to its slot
+    // (rows = keys of the block, unscaled); the reduce pass adds the slots.
+    const int slot = a.blk_slot[kt];
+    if (slot >= 0) {
+      float* part = a.blk_part + ((int64_t)bh * a.blk_nslots + slot + chunk) * 2 * BK * D;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = kblk * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          part[kl * D + db * 32 + l32] = dk[db][r];
+          part[(BK + kl) * D + db * 32 + l32] = dv[db][r];
+        }
+      }
+      return;
+    }
   }
 
   // dK = scale * acc, dV = acc; accumulator rows are keys, columns features.
@@ -768,7 +800,7 @@ template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BK = 128;
   const int n_ktiles = (a.N + BK - 1) / BK;
-  const int64_t blocks = (int64_t)n_ktiles * a.B * a.Hkv;
+  const int64_t blocks = (int64_t)(MASK == kMaskBlocks ? a.blk_max_work : n_ktiles) * a.B * a.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (MASK != kMaskPlain) {
@@ -862,6 +894,93 @@ __global__ void __launch_bounds__(256) block_table_kernel(AttnArgs a, uint8_t* t
     const int c = a.blk_col_idx[e];
     if (c >= 0 && c < a.n_kblk) row[c] = 1;
   }
+}
+
+// The balanced work list of the key-tile pass (one workgroup of 64
+// threads): per key block the length of its query list (the same causal
+// filter as build_query_block_list), its chunk count, the work items and the
+// partial-sum slots of the blocks that are cut.  The chunks of cut blocks
+// (the longest items) come first in the list, so that none of them starts
+// last.
+__global__ void __launch_bounds__(64) block_work_kernel(AttnArgs a, int causal, int* work, int* slot, int* nch) {
+  const int lane = threadIdx.x;
+  // pass 0 places the chunks of cut blocks, pass 1 the uncut blocks
+  int carry = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int base = 0; base < a.n_kblk; base += 64) {
+      const int c = base + lane;
+      int count = 0;
+      if (c < a.n_kblk) {
+        for (int r = causal ? c : 0; r < a.n_qblk; ++r) count += a.blk_table[(int64_t)r * a.n_kblk + c] != 0;
+      }
+      const int n = c < a.n_kblk ? max(1, (count + a.blk_chunk - 1) / a.blk_chunk) : 0;
+      const int mine = (pass == 0) ? (n > 1 ? n : 0) : (n == 1 ? 1 : 0);
+      int incl = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __builtin_amdgcn_ds_bpermute((int)(((unsigned)lane - (unsigned)o) << 2), incl);
+        if (lane >= o) incl += t;
+      }
+      const int w0 = carry + incl - mine;   // exclusive position
+      if (mine > 0) {
+        for (int k = 0; k < mine; ++k) work[1 + w0 + k] = c | (k << 16);
+      }
+      if (c < a.n_kblk) {
+        if (pass == 0) {
+          nch[c] = n;
+          slot[c] = n > 1 ? w0 : -1;   // the cut blocks' items and slots share positions
+        }
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  if (lane == 0) work[0] = carry;
+}
+
+// Sums the slots of each cut key block in chunk order and writes bf16 dK
+// (times scale) and dV; one workgroup per (batch, key/value head, key block).
+template <int D>
+__global__ void __launch_bounds__(256) block_reduce_kernel(AttnArgs a) {
+  constexpr int BK = 128;
+  const int c = blockIdx.x % a.n_kblk;
+  const int bh = blockIdx.x / a.n_kblk;
+  const int slot = a.blk_slot[c];
+  if (slot < 0) return;
+  const int n = a.blk_nch[c];
+  const int b = bh / a.Hkv;
+  const int hk = bh - b * a.Hkv;
+  const int64_t kv_base = ((int64_t)b * a.Hkv + hk) * a.N * D;
+  const float* part = a.blk_part + ((int64_t)bh * a.blk_nslots + slot) * 2 * BK * D;
+  for (int e = threadIdx.x; e < BK * D; e += 256) {
+    const int kl = e / D;
+    const int key = c * BK + kl;
+    if (key >= a.N) break;
+    float sk = 0.f, sv = 0.f;
+    for (int t = 0; t < n; ++t) {
+      sk += part[(int64_t)t * 2 * BK * D + e];
+      sv += part[(int64_t)t * 2 * BK * D + BK * D + e];
+    }
+    const int64_t off = kv_base + (int64_t)key * D + (e - kl * D);
+    ((uint16_t*)a.dk)[off] = (uint16_t)(pack_bf16x2(sk * a.scale, 0.f) & 0xffffu);
+    ((uint16_t*)a.dv)[off] = (uint16_t)(pack_bf16x2(sv, 0.f) & 0xffffu);
+  }
+}
+
+hipError_t launch_block_work(const AttnArgs& a, bool causal, int* work, int* slot, int* nch, hipStream_t stream) {
+  if (a.n_kblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(block_work_kernel, dim3(1), dim3(64), 0, stream, a, causal ? 1 : 0, work, slot, nch);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_reduce(const AttnArgs& a, int d, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.B * a.Hkv * a.n_kblk;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (d == 128) hipLaunchKernelGGL(block_reduce_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(block_reduce_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_block_table(const AttnArgs& a, uint8_t* table, hipStream_t stream) {

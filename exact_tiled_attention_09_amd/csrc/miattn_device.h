@@ -79,6 +79,20 @@ struct AttnArgs {
   int n_qblk;
   int n_kblk;
   const uint8_t* blk_table;
+  // Backward key-tile pass over a block list, split for balance: a key block
+  // listed by more than blk_chunk query blocks is cut into chunks of
+  // blk_chunk query blocks, one workgroup each.  blk_work[0] = number of work
+  // items, blk_work[1 + w] = key block | (chunk << 16); blk_slot[c] = first
+  // partial-sum slot of key block c (-1 when it is not cut), blk_nch[c] its
+  // chunk count; blk_part holds fp32 partial dK and dV per (batch, key/value
+  // head, slot): [B * Hkv][blk_nslots][2][128][D].
+  const int* blk_work;
+  const int* blk_slot;
+  const int* blk_nch;
+  float* blk_part;
+  int blk_chunk;
+  int blk_nslots;
+  int blk_max_work;
 };
 
 // Decoding against a KV cache (one query token per sequence), split along

@@ -20,6 +20,10 @@ hipError_t launch_bwd_dkdv_masked_bf16(const AttnArgs& a, int d, int mask, bool 
 hipError_t launch_bwd_dq_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream);
 // expands the block-sparse CSR list into a.blk_table (n_qblk x n_kblk bytes)
 hipError_t launch_block_table(const AttnArgs& a, uint8_t* table, hipStream_t stream);
+// balanced work list of the block-sparse key-tile pass (needs the table) and
+// the sums of the chunks of the key blocks it cut
+hipError_t launch_block_work(const AttnArgs& a, bool causal, int* work, int* slot, int* nch, hipStream_t stream);
+hipError_t launch_block_reduce(const AttnArgs& a, int d, hipStream_t stream);
 
 // split pass then merge pass of decoding against a KV cache
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t stream);

@@ -189,14 +189,19 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
                           int B, int H, int H_kv, int N, int d, float scale, int causal,
                           const int* row_ptr, const int* col_idx, int nnz, hipStream_t stream);
 
-/* Workspace bytes for attn_bwd_block_sparse: fp32 D (one per row) and the
- * list expanded to an nb x nb byte table. 0 for invalid sizes. */
-size_t attn_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d);
+/* Workspace bytes for attn_bwd_block_sparse with a list of nnz entries: fp32
+ * D (one per row), the list expanded to an nb x nb byte table, a balanced
+ * work list and fp32 partial sums for key blocks that many query blocks list.
+ * 0 for invalid sizes. */
+size_t attn_bwd_block_sparse_workspace_bytes(int B, int H, int H_kv, int N, int d, int nnz);
 
 /* Backward of attn_fwd_block_sparse; arguments as attn_bwd_gqa plus the
  * list.  The key-tile pass visits, for each key block, only the query blocks
- * that list it (read from the expanded table); dk, dv of a key block no query
- * block lists are 0. */
+ * that list it (read from the expanded table); a key block listed by more
+ * query blocks than the average (such as a global block) is split
+ * over several workgroups whose fp32 partial sums are then added in a fixed
+ * order, so the result does not depend on scheduling.  dk, dv of a key block
+ * no query block lists are 0. */
 int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
                           const void* dO, void* dq, void* dk, void* dv,
                           int B, int H, int H_kv, int N, int d, float scale, int causal,

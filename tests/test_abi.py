@@ -143,9 +143,11 @@ def test_window_and_block_sparse_validation():
     assert sp(512, NULL, FAKE, 4) == -1            # no row pointers
     assert sp(512, FAKE, NULL, 4) == -1            # entries but no column indices
     assert sp(512, FAKE, FAKE, -1) == -1
-    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 131072 + 1, 64) == 0
+    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 131072 + 1, 64, 4) == 0
+    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 3, 512, 64, 4) == 0
+    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 512, 64, -1) == 0
     nb = 4  # N = 512
-    ws = lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 512, 64)
+    ws = lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 512, 64, 4)
     assert ws >= lib.attn_bwd_workspace_bytes(1, 8, 512, 64) + nb * nb
     bsp = lambda wsb: lib.attn_bwd_block_sparse(*([FAKE] * 9), 1, 8, 2, 512, 64, 0.125, 1, FAKE, FAKE, 4, FAKE,
                                                 wsb, NULL)

@@ -68,7 +68,8 @@ def _run_sparse(lib, inp, scale, causal, row_ptr, col_idx):
     ci = torch.from_numpy(np.asarray(col_idx, np.int32)).cuda()
     lib.attn_fwd_block_sparse(q, k, v, o, lse, scale, causal, rp, ci)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(lib.attn_bwd_block_sparse_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.attn_bwd_block_sparse_workspace_bytes(B, H, k.shape[1], N, d, int(ci.numel())),
+                     dtype=torch.uint8, device="cuda")
     lib.attn_bwd_block_sparse(q, k, v, o, lse, do, dq, dk, dv, scale, causal, rp, ci, ws)
     torch.cuda.synchronize()
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
@@ -230,3 +231,24 @@ def test_block_sparse_full_size(lib):
     for name in ("o", "lse", "dq", "dk", "dv"):
         assert bool(torch.isfinite(out[name].float()).all()), f"non-finite {name}"
     _check_group_sampled(out, inp, scale, False, 0, 6, H // Hkv, seed=2, blocks=(rp, ci, BLOCK))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_cut_key_blocks(lib, causal):
+    """N = 2048 (16 blocks), block 0 global plus a local band: block 0 is
+    listed by all 16 query blocks, about four times the average, so the
+    key-tile pass cuts it into chunks whose partial sums are added in a fixed
+    order.  Whole comparison with the oracle, and a second run bit for bit
+    equal to the first."""
+    import torch
+    nb = 16
+    rows = [sorted({0} | {c for c in (r - 1, r, r + 1) if 0 <= c < nb}) for r in range(nb)]
+    rp, ci = _csr(rows)
+    inp = dense_inputs(1, 4, 2048, 128, "bf16", seed=31, kv_heads=2)
+    scale = 1 / math.sqrt(128)
+    out = _run_sparse(lib, inp, scale, causal, rp, ci)
+    out2 = _run_sparse(lib, inp, scale, causal, rp, ci)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(out[name], out2[name]), name
+    ref = A.gqa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, blocks=(rp, ci, BLOCK))
+    _check(out, ref)
