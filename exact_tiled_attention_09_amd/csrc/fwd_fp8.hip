@@ -6,7 +6,8 @@
 // Quantizers (HBM-bound, one pass each):
 //  * rows: Q or K [B, H, N, 128] bf16 -> codes of the same shape and one fp32
 //    scale per 64-row block (one workgroup per block);
-//  * V: one scale per (batch, head) (a per-head max, then the codes), the
+//  * V: one scale per (batch, head) (per-tile maxima, their max per head,
+//    then the codes; no atomics), the
 //    codes stored per 64-key tile transposed, [B, H, N/64, 128, 64], with the
 //    keys of a tile in the order in which a lane finds them in its score
 //    accumulators, so that P needs no shuffle before the P V product.
@@ -22,8 +23,8 @@
 // scale * s_q * s_k of the tile pair inside the softmax's single FMA.  P is
 // rounded to E4M3 after multiplying by 2^6 with the reference max allowed to
 // lag by 2 (base-2 units): P * 2^6 lies in [2^-6, 2^8] for every P >= 2^-12,
-// all normal E4M3 values.  The epilogue divides by 2^6 * l and multiplies by
-// the head's V scale.
+// all normal E4M3 values; the 2^6 is folded into the exponent, so l carries
+// it too.  The epilogue divides by l and multiplies by the head's V scale.
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
@@ -34,7 +35,7 @@ namespace miattn {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kFp8Max = 448.0f;
-constexpr float kPScale = 64.0f;        // 2^6
+constexpr float kPScaleLog2 = 6.0f;     // P is rounded to E4M3 as P * 2^6
 constexpr float kLazyMaxFp8 = 2.0f;     // P <= 2^2, so P * 2^6 <= 256 < 448
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -112,16 +113,14 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a, int nb) {
   }
 }
 
-// scales[i] = 0 (the per-head maxima are then taken with atomic max on the
-// bit patterns, which order like the values for non-negative floats)
-__global__ void __launch_bounds__(256) zero_kernel(float* p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0.f;
-}
-
+// Per-head V scale in two steps without atomics: each 64-key tile's max goes
+// to the first word of that tile's region of the output codes (overwritten by
+// the codes afterwards), then one wave per (batch, head) takes the max over
+// its tiles and writes the scale.
 template <int D>
-__global__ void __launch_bounds__(256) head_amax_kernel(QuantArgs a, int nt) {
+__global__ void __launch_bounds__(256) tile_amax_kernel(QuantArgs a, int nt) {
   constexpr int PER = 64 * D / 256 / 8;
+  __shared__ float s_max[4];
   const int bh = blockIdx.x / nt;
   const int t = blockIdx.x - bh * nt;
   const int rows = min(64, a.N - t * 64);
@@ -140,7 +139,21 @@ __global__ void __launch_bounds__(256) head_amax_kernel(QuantArgs a, int nt) {
     }
   }
   amax = wave_max64(amax);
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)(a.scales + bh), __builtin_bit_cast(unsigned int, amax));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *(float*)(a.x8 + ((int64_t)bh * nt + t) * (int64_t)D * 64) =
+        fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) head_scale_kernel(QuantArgs a, int nt) {
+  const int bh = blockIdx.x;  // one wave per (batch, head), lanes over tiles
+  float amax = 0.f;
+  for (int t = threadIdx.x; t < nt; t += 64)
+    amax = fmaxf(amax, *(const float*)(a.x8 + ((int64_t)bh * nt + t) * (int64_t)D * 64));
+  amax = wave_max64(amax);
+  if (threadIdx.x == 0) a.scales[bh] = amax == 0.f ? 1.f : amax / kFp8Max;
 }
 
 // Codes of one 64-key tile of V, transposed: out[f * 64 + p] = code of key
@@ -162,8 +175,7 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(QuantArgs a, int nt) {
     *(u32x4*)(tile + r * LD + col) = v;
   }
   __syncthreads();
-  const float amax = a.scales[bh];
-  const float s = amax == 0.f ? 1.f : amax / kFp8Max;
+  const float s = a.scales[bh];
   uint8_t* dst = a.x8 + ((int64_t)bh * nt + t) * (int64_t)D * 64;
   // one output word = 4 consecutive positions p0..p0+3 = keys k(p0)..k(p0)+3
   for (int w = tid; w < D * 16; w += 256) {
@@ -177,14 +189,6 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(QuantArgs a, int nt) {
     uint32_t word = cvt_fp8x2<false>(x0, x1, 0u);
     word = cvt_fp8x2<true>(x2, x3, word);
     *(uint32_t*)(dst + f * 64 + p0) = word;
-  }
-}
-
-__global__ void __launch_bounds__(256) amax_to_scale_kernel(float* p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) {
-    const float amax = p[i];
-    p[i] = amax == 0.f ? 1.f : amax / kFp8Max;
   }
 }
 
@@ -332,7 +336,9 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
     const float m_new = (mx > m + kLazyMaxFp8) ? mx : m;
     const bool dead = m_new == kNegInf;
     const float alpha = dead ? 1.f : fast_exp2(m - m_new);
-    const float mu = dead ? 0.f : m_new;
+    // exp2 returns P * 2^6 directly (the scaling folded into the exponent);
+    // l then carries the same factor, removed exactly in the epilogue
+    const float mu = dead ? 0.f : m_new - kPScaleLog2;
     float rs = 0.f;
     uint32_t w[8];
 #pragma unroll
@@ -345,8 +351,8 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
           e[i] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + i], cc, -mu));
           rs += e[i];
         }
-        uint32_t x = cvt_fp8x2<false>(e[0] * kPScale, e[1] * kPScale, 0u);
-        w[kb * 4 + q4] = cvt_fp8x2<true>(e[2] * kPScale, e[3] * kPScale, x);
+        uint32_t x = cvt_fp8x2<false>(e[0], e[1], 0u);
+        w[kb * 4 + q4] = cvt_fp8x2<true>(e[2], e[3], x);
       }
     p8 = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
     l = alpha * l + rs;
@@ -391,13 +397,13 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   }
   for (int t = jw_last + 1; t <= ntiles; ++t) end_interval(t);
 
-  // O = O~ * s_v / (2^6 l), LSE = ln 2 * (m + log2 l)
+  // l holds 2^6 times the row sum: O = O~ * s_v / l, LSE = ln 2 * (m + log2 l - 6)
   uint16_t* __restrict__ op = (uint16_t*)a.o + (int64_t)bh * len * D;
   const float lt = wave_sum_halves(l);
   const int qi = q_wave0 + l32;
   if (qi < len) {
     const bool dead = (m == kNegInf) || !(lt > 0.f);
-    const float inv = dead ? 0.f : a.v_scale[bhk] / (kPScale * lt);
+    const float inv = dead ? 0.f : a.v_scale[bhk] / lt;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -407,7 +413,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
                     pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
         *(u32x2*)(op + (int64_t)qi * D + db * 32 + g * 8 + hi * 4) = wv;
       }
-    if (hi == 0) a.lse[(int64_t)bh * len + qi] = dead ? kNegInf : (m + fast_log2(lt)) * kLn2;
+    if (hi == 0) a.lse[(int64_t)bh * len + qi] = dead ? kNegInf : (m + fast_log2(lt) - kPScaleLog2) * kLn2;
   }
 }
 
@@ -430,11 +436,9 @@ hipError_t launch_quant_vt_fp8(const void* v, void* v8t, float* scales, int BH, 
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   QuantArgs q = {(const uint16_t*)v, (uint8_t*)v8t, scales, BH, N};
-  const unsigned sb = (unsigned)((BH + 255) / 256);
-  hipLaunchKernelGGL(zero_kernel, dim3(sb), dim3(256), 0, stream, scales, BH);
-  hipLaunchKernelGGL(head_amax_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, q, nt);
+  hipLaunchKernelGGL(tile_amax_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, q, nt);
+  hipLaunchKernelGGL(head_scale_kernel<128>, dim3((unsigned)BH), dim3(64), 0, stream, q, nt);
   hipLaunchKernelGGL(quant_vt_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, q, nt);
-  hipLaunchKernelGGL(amax_to_scale_kernel, dim3(sb), dim3(256), 0, stream, scales, BH);
   return hipGetLastError();
 }
 

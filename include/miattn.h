@@ -242,7 +242,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
  * head) and v8t codes [B,H,ceil(N/64),128,64]: tile t, feature f, position p
  * holds key 64t + k(p), k(p) = 32 (p%32/16) + 8 (p%16/4) + 4 (p/32) + p%4,
  * keys past N coded 0 (the order in which the forward's score accumulators
- * hold a tile's keys).  Queues four small kernels; scales is overwritten. */
+ * hold a tile's keys).  Queues three kernels: per-tile maxima (kept in v8t
+ * until the codes overwrite them), the per-head scale, the codes. */
 int attn_quantize_fp8_rows(const void* x, unsigned char* x8, float* scales, int B, int H, int N, int d,
                            hipStream_t stream);
 int attn_quantize_fp8_vt(const void* v, unsigned char* v8t, float* scales, int B, int H, int N, int d,
