@@ -1,0 +1,50 @@
+"""Host-side logic of bench.py, CPU only: the FLOP accounting of the masked
+workloads counts exactly the (query, key) pairs the oracle's mask keeps, and
+the block patterns are valid CSR lists."""
+import numpy as np
+import pytest
+
+import bench
+from oracle import attention as A
+
+
+def _oracle_pairs(cfg):
+    N = cfg["N"]
+    mask = bench.oracle_mask(cfg)
+    vis = A.visible_mask(np.arange(N), N, cfg["causal"], None, mask.get("window"), mask.get("blocks"))
+    return int(vis.sum())
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(N=300, causal=True, window=(63, 0)),
+    dict(N=300, causal=False, window=(10, 25)),
+    dict(N=300, causal=False, window=(-1, 7)),
+    dict(N=256, causal=True),
+    dict(N=256, causal=False),
+    dict(N=640, causal=False, blocks="global+local+strided16"),
+    dict(N=2048 + 37, causal=True, blocks="global+local+strided16"),
+])
+def test_visible_pairs_match_the_oracle_mask(cfg):
+    assert bench.visible_pairs(cfg) == _oracle_pairs(cfg)
+
+
+def test_flop_accounting():
+    dense = dict(B=2, H=3, N=128, d=64, causal=False)
+    f, b = bench.workload_flops(dense)
+    assert f == 4.0 * 2 * 3 * 128 * 128 * 64 and b == 2.5 * f
+    win = dict(B=1, H=2, N=300, d=64, causal=True, window=(63, 0))
+    f, b = bench.workload_flops(win)
+    assert f == 4.0 * 1 * 2 * 64 * _oracle_pairs(win) and b == 2.5 * f
+
+
+def test_bench_workloads_are_well_formed():
+    for name, cfg in bench.WORKLOADS.items():
+        if "blocks" in cfg:
+            rp, ci, blk = bench.oracle_mask(cfg)["blocks"]
+            nb = -(-cfg["N"] // blk)
+            assert len(rp) == nb + 1 and rp[0] == 0 and rp[-1] == len(ci)
+            assert np.all(np.diff(rp) >= 0) and ci.min() >= 0 and ci.max() < nb
+        if "Hkv" in cfg:
+            assert cfg["H"] % cfg["Hkv"] == 0
+    assert bench.DEFAULT in bench.WORKLOADS
+    assert set(bench.DECODE_WORKLOADS).isdisjoint(bench.WORKLOADS)
