@@ -551,11 +551,26 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = wave_max_halves(mx) * cc;
-    const float m_new = (mx > m + kLazyMax) ? mx : m;
-    const bool dead = m_new == kNegInf;  // no visible key yet for this row
-    const float alpha = dead ? 1.f : fast_exp2(m - m_new);
-    const float mu = dead ? 0.f : m_new;
+    mx *= cc;
+    // The reference of a row moves only when the tile's row max exceeds it by
+    // more than kLazyMax.  While no lane's half of a row does, the wave skips
+    // the exchange between halves and the rescale (the common case after the
+    // first tiles); a row with no reference yet (m = -inf) and a visible key
+    // always takes the update.
+    if (wave_any(!(mx <= m + kLazyMax))) {
+      mx = wave_max_halves(mx);
+      const float m_new = (mx > m + kLazyMax) ? mx : m;
+      const bool dead = m_new == kNegInf;  // no visible key yet for this row
+      const float alpha = dead ? 1.f : fast_exp2(m - m_new);
+      l *= alpha;
+      m = m_new;
+      if (wave_any(alpha != 1.f)) {
+        const float a_ = pin_in_branch(alpha);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= a_;
+      }
+    }
+    const float mu = m == kNegInf ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -569,13 +584,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
         }
         p[kb * 2 + t] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       }
-    l = alpha * l + rs;
-    m = m_new;
-    if (wave_any(alpha != 1.f)) {
-      const float a_ = pin_in_branch(alpha);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= a_;
-    }
+    l += rs;
   };
 
   // Start of interval t: fetch K_{t+2} and V_{t+1} (and the flags of tile
