@@ -151,6 +151,18 @@ def test_varlen_ragged(lib, causal, padded, d):
         assert np.array_equal(g_rows, np.zeros_like(g_rows))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_empty_sequences(lib, causal):
+    """Zero-length sequences first, in the middle and last of a packed batch:
+    their workgroups exit at once and the neighbours' rows are unaffected."""
+    print(f"[case] varlen empty sequences causal={causal}", flush=True)
+    inp = varlen_inputs(6, 1, 1, 2, 128, "bf16", seed=11, lengths=[0, 70, 0, 0, 129, 0])
+    assert int(inp["cu_seqlens"][-1]) == 199
+    out = _run_varlen(lib, inp, 128 ** -0.5, causal)
+    ref = A.varlen_backward(inp["q"], inp["k"], inp["v"], inp["do"], inp["cu_seqlens"], 128 ** -0.5, causal)
+    _check(out, ref, "bf16")
+
+
 def test_whole_sequence_padded(lib):
     """A sequence whose keys are all padded: every row is fully masked, even
     without a causal mask, and its K/V receive no gradient."""
