@@ -149,10 +149,16 @@ struct SparsePlan {
 SparsePlan sparse_plan(int B, int H, int H_kv, int N, int d, int nnz) {
   SparsePlan p;
   p.nb = (N + miattn::kSparseBlock - 1) / miattn::kSparseBlock;
-  const int avg = (nnz + p.nb - 1) / p.nb;
+  // The per-key-block lists come from the expanded table, so they hold at
+  // most nb * nb entries in total whatever nnz says (repeats and
+  // out-of-range entries drop out); planning with the smaller bound keeps
+  // every count below 2^21.
+  const int64_t cap = (int64_t)p.nb * p.nb;
+  const int L = (int)((int64_t)nnz < cap ? (int64_t)nnz : cap);
+  const int avg = (L + p.nb - 1) / p.nb;
   p.chunk = avg > 4 ? avg : 4;
-  p.max_work = p.nb + (nnz + p.chunk - 1) / p.chunk;
-  p.max_slots = (2 * nnz + p.chunk - 1) / p.chunk + 1;
+  p.max_work = p.nb + (L + p.chunk - 1) / p.chunk;
+  p.max_slots = (2 * L + p.chunk - 1) / p.chunk + 1;
   const int64_t rows = (int64_t)B * H * N;
   p.off_table = workspace_bytes_for(rows);
   p.off_work = p.off_table + sparse_table_bytes(N);

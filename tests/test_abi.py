@@ -152,6 +152,13 @@ def test_window_and_block_sparse_validation():
     bsp = lambda wsb: lib.attn_bwd_block_sparse(*([FAKE] * 9), 1, 8, 2, 512, 64, 0.125, 1, FAKE, FAKE, 4, FAKE,
                                                 wsb, NULL)
     assert bsp(ws - 1) == -1
+    # A list longer than nb * nb entries (repeats) plans like nb * nb entries;
+    # nnz near INT_MAX must not overflow the plan.
+    full = lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 512, 64, nb * nb)
+    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 512, 64, 1000) == full
+    assert lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 512, 64, 2**31 - 1) == full
+    big = lib.attn_bwd_block_sparse_workspace_bytes(1, 8, 2, 131072, 64, 2**31 - 1)
+    assert 0 < big < 1 << 40
 
 
 def test_decode_validation():
