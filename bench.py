@@ -25,6 +25,7 @@ Prints ONE JSON line on stdout (progress goes to stderr).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -163,6 +164,22 @@ def measured_traffic(kernel_label, workload):
     return int(k["hbm_read_bytes"] + k["hbm_write_bytes"])
 
 
+class no_gc:
+    """The timed region runs with Python's garbage collector off: a full
+    collection while the host is enqueueing would let the GPU drain its queue
+    and idle, and the idle time would land inside one stage's events."""
+
+    def __enter__(self):
+        self.was = gc.isenabled()
+        gc.collect()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        if self.was:
+            gc.enable()
+        return False
+
+
 def cpu_baseline(inp, cfg, scale, budget_s=10.0):
     """The fp64 oracle, forward + backward, on whole (b, h) heads of the same
     inputs, head after head until about ``budget_s`` seconds of host time
@@ -232,11 +249,12 @@ def run_fp8(args, cfg):
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for ev in events:
-        step(ev)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        t0 = time.perf_counter()
+        for ev in events:
+            step(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     q_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
     f_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
     f_fwd, _ = flops(B, H, N, d, causal)
@@ -292,13 +310,14 @@ def run_decode(args, cfg):
         M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
     torch.cuda.synchronize()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e0, e1 in events:
-        e0.record(stream)
-        M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        t0 = time.perf_counter()
+        for e0, e1 in events:
+            e0.record(stream)
+            M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in events)
     nbytes = 2 * B * Hkv * N * d * 2 + 2 * B * H * d * 2 + B * H * 4
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -464,11 +483,12 @@ def main(argv=None):
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     per = {"fwd": [], "bwd_prep": [], "bwd_dkdv": [], "bwd_dq": [], "bwd": [], "step": []}
     for ev in events:

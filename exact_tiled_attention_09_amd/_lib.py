@@ -103,6 +103,31 @@ def _check(fn: str, status: int):
         raise MiattnError(fn, status, load().miattn_status_string(status).decode())
 
 
+_DTYPES = {}
+
+
+def _dtype(name: str):
+    if not _DTYPES:
+        import torch
+        _DTYPES.update(bfloat16=torch.bfloat16, float32=torch.float32, int32=torch.int32, uint8=torch.uint8)
+    return _DTYPES[name]
+
+
+def _expect(fn: str, *specs):
+    """Each spec is (name, tensor, shape tuple, dtype name): the library sees
+    raw pointers, so a tensor of the wrong shape or dtype would make its
+    kernels read or write past the buffer; refuse it here, before any launch.
+    (torch.Size compares with a tuple in C and dtypes by identity: the check
+    stays far below a kernel launch in host time.)"""
+    for name, t, shape, dtype in specs:
+        if t is None or t.shape != shape or t.dtype is not _dtype(dtype):
+            if t is None:
+                raise ValueError(f"{fn}: {name} is required")
+            if t.shape != shape:
+                raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+            raise ValueError(f"{fn}: {name} is {t.dtype}, expected torch.{dtype}")
+
+
 def _dense_dims(q):
     if q.dim() != 4:
         raise ValueError("dense tensors are [B, H, N, d]")
@@ -118,8 +143,17 @@ def miattn_status_string(status: int) -> str:
     return load().miattn_status_string(status).decode()
 
 
+def _dense_specs(fn, dtype, B, H, N, d, **tensors):
+    shapes = {"lse": (B, H, N)}
+    specs = []
+    for name, t in tensors.items():
+        specs.append((name, t, shapes.get(name, (B, H, N, d)), "float32" if name == "lse" else dtype))
+    _expect(fn, *specs)
+
+
 def attn_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_fwd", "bfloat16", B, H, N, d, q=q, k=k, v=v, o=o, lse=lse)
     _check("attn_fwd", load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                        float(scale), int(bool(causal)), _stream(stream)))
 
@@ -130,6 +164,7 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
     B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_bwd", "bfloat16", B, H, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv)
     _check("attn_bwd", load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
                                        _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -138,6 +173,7 @@ def attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, worksp
 
 def attn_bwd_preprocess(o, dO, workspace, stream=None):
     B, H, N, d = _dense_dims(o)
+    _dense_specs("attn_bwd_preprocess", "bfloat16", B, H, N, d, o=o, dO=dO)
     _check("attn_bwd_preprocess", load().attn_bwd_preprocess(_ptr(o), _ptr(dO), B, H, N, d, _ptr(workspace),
                                                              workspace.numel() * workspace.element_size(),
                                                              _stream(stream)))
@@ -145,6 +181,7 @@ def attn_bwd_preprocess(o, dO, workspace, stream=None):
 
 def attn_bwd_dkdv(q, k, v, lse, dO, dk, dv, scale: float, causal: bool, workspace, stream=None):
     B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_bwd_dkdv", "bfloat16", B, H, N, d, q=q, k=k, v=v, lse=lse, dO=dO, dk=dk, dv=dv)
     _check("attn_bwd_dkdv", load().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(dk),
                                                  _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -153,6 +190,7 @@ def attn_bwd_dkdv(q, k, v, lse, dO, dk, dv, scale: float, causal: bool, workspac
 
 def attn_bwd_dq(q, k, v, lse, dO, dq, scale: float, causal: bool, workspace, stream=None):
     B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_bwd_dq", "bfloat16", B, H, N, d, q=q, k=k, v=v, lse=lse, dO=dO, dq=dq)
     _check("attn_bwd_dq", load().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(dq), B, H, N, d,
                                              float(scale), int(bool(causal)), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -165,14 +203,34 @@ def _gqa_dims(q, k):
     return B, H, int(k.shape[1]), N, d
 
 
+def _gqa_specs(fn, B, H, Hkv, N, d, **tensors):
+    kv_names = ("k", "v", "dk", "dv")
+    specs = []
+    for name, t in tensors.items():
+        if name == "lse":
+            specs.append((name, t, (B, H, N), "float32"))
+        else:
+            specs.append((name, t, (B, Hkv if name in kv_names else H, N, d), "bfloat16"))
+    _expect(fn, *specs)
+
+
+def _block_list_specs(fn, N, row_ptr, col_idx):
+    nqb = (N + 127) // 128
+    if col_idx is None or col_idx.dim() != 1:
+        raise ValueError(f"{fn}: col_idx is a 1-D int32 tensor")
+    _expect(fn, ("row_ptr", row_ptr, (nqb + 1,), "int32"), ("col_idx", col_idx, (int(col_idx.numel()),), "int32"))
+
+
 def attn_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     B, H, Hkv, N, d = _gqa_dims(q, k)
+    _gqa_specs("attn_fwd_gqa", B, H, Hkv, N, d, q=q, k=k, v=v, o=o, lse=lse)
     _check("attn_fwd_gqa", load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
                                                float(scale), int(bool(causal)), _stream(stream)))
 
 
 def attn_bwd_gqa(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
     B, H, Hkv, N, d = _gqa_dims(q, k)
+    _gqa_specs("attn_bwd_gqa", B, H, Hkv, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv)
     _check("attn_bwd_gqa", load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
                                                int(bool(causal)), _ptr(workspace),
@@ -182,6 +240,7 @@ def attn_bwd_gqa(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, wo
 def attn_fwd_window(q, k, v, o, lse, scale: float, causal: bool, window_left: int, window_right: int,
                     stream=None):
     B, H, Hkv, N, d = _gqa_dims(q, k)
+    _gqa_specs("attn_fwd_window", B, H, Hkv, N, d, q=q, k=k, v=v, o=o, lse=lse)
     _check("attn_fwd_window", load().attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
                                                      float(scale), int(bool(causal)), int(window_left),
                                                      int(window_right), _stream(stream)))
@@ -190,6 +249,7 @@ def attn_fwd_window(q, k, v, o, lse, scale: float, causal: bool, window_left: in
 def attn_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, window_left: int,
                     window_right: int, workspace, stream=None):
     B, H, Hkv, N, d = _gqa_dims(q, k)
+    _gqa_specs("attn_bwd_window", B, H, Hkv, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv)
     _check("attn_bwd_window", load().attn_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
                                                      int(bool(causal)), int(window_left), int(window_right),
@@ -200,6 +260,8 @@ def attn_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool,
 def attn_fwd_block_sparse(q, k, v, o, lse, scale: float, causal: bool, row_ptr, col_idx, stream=None):
     """row_ptr, col_idx: int32 device tensors (the CSR block list)."""
     B, H, Hkv, N, d = _gqa_dims(q, k)
+    _gqa_specs("attn_fwd_block_sparse", B, H, Hkv, N, d, q=q, k=k, v=v, o=o, lse=lse)
+    _block_list_specs("attn_fwd_block_sparse", N, row_ptr, col_idx)
     _check("attn_fwd_block_sparse",
            load().attn_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
                                         float(scale), int(bool(causal)), _ptr(row_ptr), _ptr(col_idx),
@@ -213,6 +275,8 @@ def attn_bwd_block_sparse_workspace_bytes(B: int, H: int, H_kv: int, N: int, d: 
 def attn_bwd_block_sparse(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, row_ptr, col_idx,
                           workspace, stream=None):
     B, H, Hkv, N, d = _gqa_dims(q, k)
+    _gqa_specs("attn_bwd_block_sparse", B, H, Hkv, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv)
+    _block_list_specs("attn_bwd_block_sparse", N, row_ptr, col_idx)
     _check("attn_bwd_block_sparse",
            load().attn_bwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
                                         _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)),
@@ -233,6 +297,11 @@ def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_seqlens, worksp
     Hkv, N = int(k_cache.shape[1]), int(k_cache.shape[2])
     if int(k_cache.shape[0]) != B or int(k_cache.shape[3]) != d:
         raise ValueError("the caches must have the B and d of q")
+    _expect("attn_decode", ("q", q, (B, H, d), "bfloat16"), ("k_cache", k_cache, (B, Hkv, N, d), "bfloat16"),
+            ("v_cache", v_cache, (B, Hkv, N, d), "bfloat16"), ("o", o, (B, H, d), "bfloat16"),
+            ("lse", lse, (B, H), "float32"))
+    if cache_seqlens is not None:
+        _expect("attn_decode", ("cache_seqlens", cache_seqlens, (B,), "int32"))
     sl = None if cache_seqlens is None else _ptr(cache_seqlens)
     _check("attn_decode", load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, H, Hkv,
                                              N, d, float(scale), sl, _ptr(workspace),
@@ -242,6 +311,8 @@ def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_seqlens, worksp
 def attn_quantize_fp8_rows(x, x8, scales, stream=None):
     """x bf16 [B, H, N, d] -> x8 uint8 [B, H, N, d], scales fp32 [B, H, ceil(N/64)]."""
     B, H, N, d = _dense_dims(x)
+    _expect("attn_quantize_fp8_rows", ("x", x, (B, H, N, d), "bfloat16"), ("x8", x8, (B, H, N, d), "uint8"),
+            ("scales", scales, (B, H, (N + 63) // 64), "float32"))
     _check("attn_quantize_fp8_rows", load().attn_quantize_fp8_rows(_ptr(x), _ptr(x8), _ptr(scales), B, H, N, d,
                                                                    _stream(stream)))
 
@@ -249,13 +320,20 @@ def attn_quantize_fp8_rows(x, x8, scales, stream=None):
 def attn_quantize_fp8_vt(v, v8t, scales, stream=None):
     """v bf16 [B, H, N, d] -> v8t uint8 [B, H, ceil(N/64), d, 64], scales fp32 [B, H]."""
     B, H, N, d = _dense_dims(v)
+    _expect("attn_quantize_fp8_vt", ("v", v, (B, H, N, d), "bfloat16"),
+            ("v8t", v8t, (B, H, (N + 63) // 64, d, 64), "uint8"), ("scales", scales, (B, H), "float32"))
     _check("attn_quantize_fp8_vt", load().attn_quantize_fp8_vt(_ptr(v), _ptr(v8t), _ptr(scales), B, H, N, d,
                                                                _stream(stream)))
 
 
 def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, o, lse, scale: float, causal: bool, stream=None):
     B, H, N, d = _dense_dims(q8)
-    Hkv = int(k8.shape[1])
+    Hkv = int(k8.shape[1]) if k8 is not None and k8.dim() == 4 else -1
+    nb = (N + 63) // 64
+    _expect("attn_fwd_fp8", ("q8", q8, (B, H, N, d), "uint8"), ("q_scale", q_scale, (B, H, nb), "float32"),
+            ("k8", k8, (B, Hkv, N, d), "uint8"), ("k_scale", k_scale, (B, Hkv, nb), "float32"),
+            ("v8t", v8t, (B, Hkv, nb, d, 64), "uint8"), ("v_scale", v_scale, (B, Hkv), "float32"),
+            ("o", o, (B, H, N, d), "bfloat16"), ("lse", lse, (B, H, N), "float32"))
     _check("attn_fwd_fp8", load().attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8t),
                                                _ptr(v_scale), _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale),
                                                int(bool(causal)), _stream(stream)))
@@ -267,12 +345,14 @@ def attn_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def attn_fwd_f32(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_fwd_f32", "float32", B, H, N, d, q=q, k=k, v=v, o=o, lse=lse)
     _check("attn_fwd_f32", load().attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                                float(scale), int(bool(causal)), _stream(stream)))
 
 
 def attn_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
     B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_bwd_f32", "float32", B, H, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv)
     _check("attn_bwd_f32", load().attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
                                                int(bool(causal)), _ptr(workspace),
@@ -286,9 +366,21 @@ def _varlen_dims(q):
     return int(T), int(H), int(d)
 
 
+def _varlen_specs(fn, T, H, d, cu_seqlens, key_valid, **tensors):
+    if cu_seqlens is None or cu_seqlens.dim() != 1:
+        raise ValueError(f"{fn}: cu_seqlens is a 1-D int32 tensor [nseq + 1]")
+    specs = [("cu_seqlens", cu_seqlens, (int(cu_seqlens.numel()),), "int32")]
+    for name, t in tensors.items():
+        specs.append((name, t, (H, T) if name == "lse" else (T, H, d), "float32" if name == "lse" else "bfloat16"))
+    if key_valid is not None:
+        specs.append(("key_valid", key_valid, (T,), "uint8"))
+    _expect(fn, *specs)
+
+
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool,
                     key_valid=None, stream=None):
     T, H, d = _varlen_dims(q)
+    _varlen_specs("attn_fwd_varlen", T, H, d, cu_seqlens, key_valid, q=q, k=k, v=v, o=o, lse=lse)
     nseq = int(cu_seqlens.numel()) - 1
     _check("attn_fwd_varlen", load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                                      _ptr(cu_seqlens), nseq, int(max_seqlen), T, H, d,
@@ -303,6 +395,8 @@ def attn_bwd_varlen_workspace_bytes(total_tokens: int, H: int, d: int) -> int:
 def attn_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens, max_seqlen: int, scale: float, causal: bool,
                     workspace, key_valid=None, stream=None):
     T, H, d = _varlen_dims(q)
+    _varlen_specs("attn_bwd_varlen", T, H, d, cu_seqlens, key_valid, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq,
+                  dk=dk, dv=dv)
     nseq = int(cu_seqlens.numel()) - 1
     _check("attn_bwd_varlen", load().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq,
