@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   uint16_t* const sK = arena + 4 * QT_ELEMS;
   uint16_t* const sV = arena + 4 * QT_ELEMS + KV_ELEMS;
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // LSE * log2(e), +inf if dead
-  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];  // D
+  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];  // -D (the starting value of dP - D)
 
   // One workgroup per (sequence, key/value head, key tile).  With grouped
   // heads it runs the query-tile loop once for each of the G query heads
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
 #pragma unroll
     for (int n = 0; n < 2 * QCPT; ++n) issue_part(buf, n);
   };
-  // LSE (as log2, +inf when the row is dead or past the end) and D of the
+  // LSE (as log2, +inf when the row is dead or past the end) and -D of the
   // tile's rows, through registers of wave 0 (BQ = 64 rows, one per lane).
   // The raw values are loaded at the start of a step and converted only when
   // stored at its end, so the wave does not wait for the loads in between.
@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     if (wave == 0) {
       const bool out = rq >= len;
       sL[buf][lane] = (out || rl == kNegInf) ? kPosInf : rl * kLog2e;
-      sDv[buf][lane] = out ? 0.f : rd;
+      sDv[buf][lane] = out ? 0.f : -rd;
     }
   };
 
@@ -325,8 +325,15 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
         if (CAUSAL) need_mask = need_mask || (wk0 + 31 > q0 + qb * 32);
         if (MASK == kMaskWindow)
           need_mask = need_mask || (wk0 < q0 + qb * 32 + 31 - a.win_left) || (wk0 + 31 > q0 + qb * 32 + a.win_right);
-        // S and dP, their four operands read one k-step ahead.
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // S and dP - D (the dP accumulator starts at -D of its rows), their
+        // four operands read one k-step ahead.
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 nd = *(const f32x4*)(&sDv[buf][qb * 32 + g * 8 + hi * 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[g * 4 + e] = nd[e];
+        }
         bf16x8 opq[2], opk[2], opg[2], opv[2];
         auto sread = [&](int ks, int u) __attribute__((always_inline)) {
           const int off = qb * 32 * D + aoff[ks];
@@ -368,13 +375,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + g * 8 + hi * 4;
           const f32x4 lv = *(const f32x4*)(&sL[buf][ql]);
-          const f32x4 dvv = *(const f32x4*)(&sDv[buf][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = g * 4 + e;
             const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lv[e]));
             s[r] = p;
-            dp[r] = p * (dp[r] - dvv[e]);
+            dp[r] = p * dp[r];
           }
         }
         // dV += P^T dO and dK += dS^T Q, 16 query rows per MFMA; the
