@@ -141,7 +141,7 @@ def oracle_mask(cfg):
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_causal_b4_h32_n4096_d128.json")
 KERNEL_KEYS = {"fwd_stag_kernel (attn_fwd)": "fwd_stag_kernel",
                "bwd_dkdv_kernel (attn_bwd_dkdv)": "bwd_dkdv_kernel",
-               "bwd_dq_kernel (attn_bwd_dq)": "bwd_dq_kernel"}
+               "bwd_dq_kernel (attn_bwd_dq_preprocess)": "bwd_dq_kernel"}
 
 
 def measured_traffic(kernel_label, workload):
@@ -455,7 +455,7 @@ def main(argv=None):
             ev[1].record(stream)
         bwd_call()
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     def step(ev=None):
         if grouped:
@@ -465,22 +465,21 @@ def main(argv=None):
         M.attn_fwd(q, k, v, o, lse, scale, causal, stream)
         if ev is not None:
             ev[1].record(stream)
-        M.attn_bwd_preprocess(o, do, ws, stream)
+        # the backward as attn_bwd runs it: the dQ pass (which also stores D),
+        # then the dK/dV pass
+        M.attn_bwd_dq_preprocess(q, k, v, o, lse, do, dq, scale, causal, ws, stream)
         if ev is not None:
             ev[2].record(stream)
         M.attn_bwd_dkdv(q, k, v, lse, do, dk, dv, scale, causal, ws, stream)
         if ev is not None:
             ev[3].record(stream)
-        M.attn_bwd_dq(q, k, v, lse, do, dq, scale, causal, ws, stream)
-        if ev is not None:
-            ev[4].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     with no_gc():
@@ -490,15 +489,14 @@ def main(argv=None):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
-    per = {"fwd": [], "bwd_prep": [], "bwd_dkdv": [], "bwd_dq": [], "bwd": [], "step": []}
+    per = {"fwd": [], "bwd_dkdv": [], "bwd_dq": [], "bwd": [], "step": []}
     for ev in events:
         per["fwd"].append(ev[0].elapsed_time(ev[1]))
-        per["bwd"].append(ev[1].elapsed_time(ev[4]))
-        per["step"].append(ev[0].elapsed_time(ev[4]))
+        per["bwd"].append(ev[1].elapsed_time(ev[3]))
+        per["step"].append(ev[0].elapsed_time(ev[3]))
         if not grouped:
-            per["bwd_prep"].append(ev[1].elapsed_time(ev[2]))
+            per["bwd_dq"].append(ev[1].elapsed_time(ev[2]))
             per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
-            per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
     per = {k_: v_ for k_, v_ in per.items() if v_}
     mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
     med = {k_: statistics.median(v_) for k_, v_ in per.items()}
@@ -514,7 +512,6 @@ def main(argv=None):
     elem_q = B * H * N * d
     elem_kv = B * Hkv * N * d
     rows = B * H * N
-    prep_bytes = 2 * elem_q * 2 + rows * 4                          # read O, dO; write D
     fwd_bytes = 2 * elem_q * 2 + 2 * elem_kv * 2 + rows * 4         # read Q, K, V; write O, LSE
     bwd = {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
            "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2)}
@@ -524,14 +521,11 @@ def main(argv=None):
     if not grouped:
         tflops_dkdv = f_dkdv / (mean["bwd_dkdv"] * 1e-3) / 1e12
         tflops_dq = f_dq / (mean["bwd_dq"] * 1e-3) / 1e12
-        bwd.update({"prep_ms": round(mean["bwd_prep"], 4),
-                    "prep_gbps": round(prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9, 1),
-                    "prep_pct_hbm_peak": round(100 * prep_bytes / (mean["bwd_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                                               2),
-                    "dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
-                    "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2)})
+        bwd.update({"dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
+                    "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2),
+                    "dq_forms_d": True})
         kern["bwd_dkdv_kernel (attn_bwd_dkdv)"] = (mean["bwd_dkdv"], f_dkdv)
-        kern["bwd_dq_kernel (attn_bwd_dq)"] = (mean["bwd_dq"], f_dq)
+        kern["bwd_dq_kernel (attn_bwd_dq_preprocess)"] = (mean["bwd_dq"], f_dq)
     else:
         kern = {f"fwd_stag_kernel ({fwd_name})": (mean["fwd"], f_fwd)}
     dom = max(kern, key=lambda k_: kern[k_][0])

@@ -5,7 +5,7 @@ include/miattn.h); this package is its thin ctypes binding plus the build
 script.  Functions carry the C names and take device tensors:
 
     attn_fwd, attn_bwd, attn_bwd_workspace_bytes,
-    attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq,
+    attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_dq_preprocess,
     attn_fwd_gqa, attn_bwd_gqa,
     attn_fwd_window, attn_bwd_window,
     attn_fwd_block_sparse, attn_bwd_block_sparse, attn_bwd_block_sparse_workspace_bytes,
@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
+    attn_bwd_dq_preprocess,
     attn_bwd_f32,
     attn_bwd_f32_workspace_bytes,
     attn_bwd_gqa,

@@ -35,6 +35,7 @@ SIGNATURES = {
     "attn_bwd_preprocess": (_I, [_P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "attn_bwd_dkdv": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_bwd_dq": (_I, [_P] * 6 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_bwd_dq_preprocess": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_gqa": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_window": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _I, _I, _P]),
@@ -194,6 +195,15 @@ def attn_bwd_dq(q, k, v, lse, dO, dq, scale: float, causal: bool, workspace, str
     _check("attn_bwd_dq", load().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(dq), B, H, N, d,
                                              float(scale), int(bool(causal)), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_bwd_dq_preprocess(q, k, v, o, lse, dO, dq, scale: float, causal: bool, workspace, stream=None):
+    B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_bwd_dq_preprocess", "bfloat16", B, H, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq)
+    _check("attn_bwd_dq_preprocess",
+           load().attn_bwd_dq_preprocess(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), B, H, N,
+                                         d, float(scale), int(bool(causal)), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def _gqa_dims(q, k):

@@ -265,6 +265,23 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, c
   return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
 }
 
+int attn_bwd_dq_preprocess(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, void* dq, int B, int H, int N, int d, float scale, int causal,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(workspace))
+    return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if (workspace_bytes < workspace_bytes_for(rows)) return MIATTN_ERR_INVALID_ARG;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.dout = dO;
+  a.dq = dq;
+  a.dq_writes_d = 1;
+  carve(a, workspace, rows);
+  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
              void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
              size_t workspace_bytes, hipStream_t stream) {
@@ -280,9 +297,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.dk = dk;
   a.dv = dv;
   carve(a, workspace, rows);
-  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
+  // the dQ pass computes and stores D (no pre-pass); the dK/dV pass reads it
+  a.dq_writes_d = 1;
+  if (int st = hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream));
 }
 
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
@@ -312,9 +330,10 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
   a.dk = dk;
   a.dv = dv;
   carve(a, workspace, rows);
-  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream));
+  // the dQ pass computes and stores D (no pre-pass); the dK/dV pass reads it
+  a.dq_writes_d = 1;
+  if (int st = hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream));
 }
 
 int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
@@ -351,13 +370,13 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
   bool c = causal != 0;
   int mode = 0;
   if (int st = window_mode(a, N, window_left, window_right, &c, &mode)) return st;
-  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
+  a.dq_writes_d = 1;  // the dQ pass stores D for the dK/dV pass
   if (mode == miattn::kMaskPlain) {
-    if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, c, false, stream))) return st;
-    return hip_status(miattn::launch_bwd_dq_bf16(a, d, c, false, stream));
+    if (int st = hip_status(miattn::launch_bwd_dq_bf16(a, d, c, false, stream))) return st;
+    return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, c, false, stream));
   }
-  if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, mode, false, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, mode, false, stream));
+  if (int st = hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, mode, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, mode, false, stream));
 }
 
 int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
@@ -414,10 +433,13 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
   const bool c = causal != 0;
   if (int st = hip_status(miattn::launch_block_table(a, table, stream))) return st;
   if (int st = hip_status(miattn::launch_block_work(a, c, work, slot, nch, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, false, stream))) return st;
+  // The dQ pass stores D for the dK/dV pass.  A query block with an empty
+  // list stores none, and no key block's list holds it (both passes drop
+  // the same entries), so the dK/dV pass never reads it.
+  a.dq_writes_d = 1;
+  if (int st = hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, miattn::kMaskBlocks, c, stream))) return st;
   if (int st = hip_status(miattn::launch_bwd_dkdv_masked_bf16(a, d, miattn::kMaskBlocks, c, stream))) return st;
-  if (int st = hip_status(miattn::launch_block_reduce(a, d, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_masked_bf16(a, d, miattn::kMaskBlocks, c, stream));
+  return hip_status(miattn::launch_block_reduce(a, d, stream));
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int N_kv, int d) {
@@ -559,9 +581,9 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.key_valid = key_valid;
   a.total_tokens = total_tokens;
   carve(a, workspace, rows);
-  if (int st = hip_status(miattn::launch_bwd_prep_bf16(a, d, true, stream))) return st;
-  if (int st = hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, true, stream))) return st;
-  return hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, true, stream));
+  a.dq_writes_d = 1;  // the dQ pass stores D for the dK/dV pass
+  if (int st = hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, true, stream))) return st;
+  return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, true, stream));
 }
 
 }  // extern "C"

@@ -643,16 +643,48 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     // the sequence load its last row and are zeroed (no branch).
     const int qc = min(qi, sv.len - 1);
     const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+    u32x4 graw[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int64_t off = (int64_t)qc * sv.tok_stride + ks * 16 + hi * 8;
       qf[ks] = as_bf16x8(*(const u32x4*)(qp + off) & keep);
-      gf[ks] = as_bf16x8(*(const u32x4*)(gp + off) & keep);
+      graw[ks] = *(const u32x4*)(gp + off) & keep;
+      gf[ks] = as_bf16x8(graw[ks]);
     }
     // a dead or out-of-range row gets P = 0
     const float lse_raw = a.lse[sv.row_base + qc];
     const float lse2 = (!row_ok || lse_raw == kNegInf) ? kPosInf : lse_raw * kLog2e;
-    const float dd = row_ok ? a.dvec[sv.row_base + qc] : 0.f;
+    float dd;
+    if (a.dq_writes_d) {
+      // D = rowsum(dO o O) in the summation order of the D pre-pass, so both
+      // give the same bits: each 8-feature chunk in order (this lane holds
+      // chunks 2 ks + hi), the chunks as a tree (partners 8, 4, 2 chunks
+      // apart, i.e. ks apart by KS/2, KS/4, ...), then the even half plus
+      // the odd half from the lane 32 away.
+      const uint16_t* __restrict__ opp = (const uint16_t*)a.o + sv.base;
+      float part[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int64_t off = (int64_t)qc * sv.tok_stride + ks * 16 + hi * 8;
+        const u32x4 ov = *(const u32x4*)(opp + off) & keep;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc = __builtin_fmaf(bf16_bits_to_f32(ov[w] & 0xffffu), bf16_bits_to_f32(graw[ks][w] & 0xffffu), acc);
+          acc = __builtin_fmaf(bf16_bits_to_f32(ov[w] >> 16), bf16_bits_to_f32(graw[ks][w] >> 16), acc);
+        }
+        part[ks] = acc;
+      }
+#pragma unroll
+      for (int w = KS / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int ks = 0; ks < w; ++ks) part[ks] = part[ks] + part[ks + w];
+      dd = part[0] + lane_xor32(part[0]);
+      if (row_ok && hi == 0) a.dvec[sv.row_base + qi] = dd;
+      dd = row_ok ? dd : 0.f;
+    } else {
+      dd = row_ok ? a.dvec[sv.row_base + qc] : 0.f;
+    }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     barrier_vmem_n<0>();

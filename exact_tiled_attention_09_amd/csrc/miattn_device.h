@@ -93,6 +93,10 @@ struct AttnArgs {
   int blk_chunk;
   int blk_nslots;
   int blk_max_work;
+  // Nonzero: the dQ pass computes D = rowsum(dO o O) of its rows itself (from
+  // o and dout), stores it in dvec for the dK/dV pass and uses it (no D
+  // pre-pass); zero: it reads dvec.
+  int dq_writes_d;
 };
 
 // Decoding against a KV cache (one query token per sequence), split along

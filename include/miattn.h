@@ -96,9 +96,10 @@ size_t attn_bwd_f32_workspace_bytes(int B, int H, int N, int d);
  * [B,H,N,d] bf16 (fp32 accumulation, one final rounding).  workspace: at least
  * attn_bwd_workspace_bytes(B,H,N,d) bytes, 16-byte aligned, no initial
  * contents required; it is overwritten.  The LSE receives no gradient.
- * Equivalent to attn_bwd_preprocess, then attn_bwd_dkdv and attn_bwd_dq (the
- * last two are independent of each other).  The result is bitwise
- * reproducible: no output is accumulated with atomics.
+ * Runs attn_bwd_dq_preprocess, then attn_bwd_dkdv; the result equals, bit for
+ * bit, attn_bwd_preprocess followed by attn_bwd_dkdv and attn_bwd_dq (the
+ * last two independent of each other).  The result is bitwise reproducible:
+ * no output is accumulated with atomics.
  * LSE-recompute backward of "解析 FlashAttention（4）" section 五. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dO, void* dq, void* dk, void* dv,
@@ -124,6 +125,15 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
 int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dq,
                 int B, int H, int N, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stages 1 and 3 in one pass: the query-tile loop of attn_bwd_dq that first
+ * forms D = rowsum(dO o O) of its own rows ("解析 FlashAttention（4）"
+ * section 5.2), uses it and stores it in the workspace, bit for bit what
+ * attn_bwd_preprocess stores; attn_bwd_dkdv may then run on the workspace.
+ * Arguments as attn_bwd_dq plus o (from attn_fwd). */
+int attn_bwd_dq_preprocess(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, void* dq, int B, int H, int N, int d, float scale, int causal,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Forward with grouped key/value heads (grouped-query attention; H_kv = 1 is
  * multi-query attention), dense bf16.  q, o: [B,H,N,d]; k, v: [B,H_kv,N,d];

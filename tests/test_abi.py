@@ -102,6 +102,10 @@ def test_backward_rejects_small_workspace():
     need32 = lib.attn_bwd_f32_workspace_bytes(1, 2, 64, 64)
     st = lib.attn_bwd_f32(*([FAKE] * 9), 1, 2, 64, 64, 0.125, 1, FAKE, need32 - 4, NULL)
     assert st == -1
+    dqp = lambda o, ws: lib.attn_bwd_dq_preprocess(FAKE, FAKE, FAKE, o, *([FAKE] * 3), 1, 2, 64, 64, 0.125, 1,
+                                                    FAKE, ws, NULL)
+    assert dqp(FAKE, need - 4) == -1        # workspace too small
+    assert dqp(NULL, need) == -1            # no O to form D from
 
 
 def test_varlen_validation():

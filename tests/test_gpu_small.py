@@ -177,8 +177,10 @@ def test_whole_sequence_padded(lib):
 
 
 def test_backward_stages_match_attn_bwd(lib):
-    """attn_bwd == attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq, bitwise:
-    no output of the bf16 backward is accumulated with atomics."""
+    """attn_bwd == attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq ==
+    attn_bwd_dq_preprocess + attn_bwd_dkdv, bitwise (no output of the bf16
+    backward is accumulated with atomics, and the dQ pass forms D in the
+    pre-pass's summation order)."""
     import torch
     inp = dense_inputs(2, 4, 500, 128, "bf16", seed=21)
     q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
@@ -197,10 +199,20 @@ def test_backward_stages_match_attn_bwd(lib):
     torch.cuda.synchronize()
     for a_, b_ in zip(g1, g2):
         assert torch.equal(a_, b_)
+    d_pre = ws[: B * H * N * 4].clone()
     g3 = [torch.empty_like(q) for _ in range(3)]
     lib.attn_bwd(q, k, v, o, lse, do, *g3, scale, True, ws)
     torch.cuda.synchronize()
     for a_, b_ in zip(g1, g3):
+        assert torch.equal(a_, b_)
+    ws.zero_()
+    g4 = [torch.empty_like(q) for _ in range(3)]
+    lib.attn_bwd_dq_preprocess(q, k, v, o, lse, do, g4[0], scale, True, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ws[: B * H * N * 4], d_pre)   # the same D, bit for bit
+    lib.attn_bwd_dkdv(q, k, v, lse, do, g4[1], g4[2], scale, True, ws)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(g1, g4):
         assert torch.equal(a_, b_)
 
 
