@@ -106,22 +106,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int B, int H, int N, int d, float scale, int causal,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 1 of attn_bwd: D = rowsum(dO o O) in fp32 into the workspace
- * ("解析 FlashAttention（4）" section 5.2). */
+/* The D pre-pass, stage 1 of the three-stage backward (attn_bwd itself forms
+ * D inside its dQ pass, attn_bwd_dq_preprocess): D = rowsum(dO o O) in fp32
+ * into the workspace ("解析 FlashAttention（4）" section 5.2). */
 int attn_bwd_preprocess(const void* o, const void* dO, int B, int H, int N, int d,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 2 of attn_bwd: the key-tile outer loop that rebuilds P and dS and
- * writes dk and dv ("解析 FlashAttention（4）" section 5.4).  Needs stage 1 on
- * the same workspace. */
+/* The dK/dV stage of attn_bwd: the key-tile outer loop that rebuilds P and dS
+ * and writes dk and dv ("解析 FlashAttention（4）" section 5.4).  Needs D in
+ * the same workspace, from attn_bwd_preprocess or attn_bwd_dq_preprocess. */
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
                   void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 3 of attn_bwd: a query-tile outer loop that rebuilds P and dS and
- * writes dq = scale dS K ("解析 FlashAttention（4）" sections 5.3-5.4, with
- * the dQ sum taken per query tile instead of by atomic adds).  Needs stage 1
- * on the same workspace. */
+/* The dQ stage of the three-stage backward: a query-tile outer loop that
+ * rebuilds P and dS and writes dq = scale dS K ("解析 FlashAttention（4）"
+ * sections 5.3-5.4, with the dQ sum taken per query tile instead of by atomic
+ * adds).  Needs D in the same workspace (attn_bwd_preprocess). */
 int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dq,
                 int B, int H, int N, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
