@@ -163,6 +163,31 @@ def test_block_sparse_ragged(lib, pattern, N, d, causal):
         assert np.all(to_np(out["o"])[dead] == 0) and np.all(to_np(out["dq"])[dead] == 0)
 
 
+@pytest.mark.parametrize("N", [1, 17, 127, 128, 129])
+@pytest.mark.parametrize("kind", ["window(0,0)", "window(16,5)", "causal window(3)", "blocks all",
+                                  "blocks empty rows"])
+def test_masked_short_sequences(lib, kind, N):
+    """Single and partial tiles: one token, less than a tile, and lengths
+    around the 128-token block (one block ragged, one full, a second block of
+    one token)."""
+    d = 64
+    print(f"[case] short {kind} N={N}", flush=True)
+    inp = dense_inputs(1, 4, N, d, "bf16", seed=N * 11 + len(kind), kv_heads=2)
+    scale = 0.125
+    if kind.startswith("blocks"):
+        nb = -(-N // BLOCK)
+        rp, ci = _csr(_patterns(nb)["all" if kind == "blocks all" else "empty rows"])
+        causal = kind == "blocks all"
+        out = _run_sparse(lib, inp, scale, causal, rp, ci)
+        ref = A.gqa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, blocks=(rp, ci, BLOCK))
+    else:
+        left, right, causal = {"window(0,0)": (0, 0, False), "window(16,5)": (16, 5, False),
+                               "causal window(3)": (3, -1, True)}[kind]
+        out = _run_window(lib, inp, scale, causal, left, right)
+        ref = A.gqa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, window=(left, right))
+    _check(out, ref)
+
+
 def test_block_sparse_ignores_out_of_range_entries(lib):
     """Entries outside [0, nb) are skipped: the result is that of the list
     without them."""
