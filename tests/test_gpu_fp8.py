@@ -127,7 +127,7 @@ def _check(o, lse, q, k, v, scale, causal, mse_bar=None):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N,Hkv", [(64, 4), (200, 2), (333, 4), (1000, 1)])
+@pytest.mark.parametrize("N,Hkv", [(1, 2), (17, 4), (64, 4), (200, 2), (333, 4), (1000, 1)])
 def test_fp8_forward_ragged(lib, N, Hkv, causal):
     print(f"[case] fp8 fwd N={N} Hkv={Hkv} causal={causal}", flush=True)
     inp = dense_inputs(2, 4, N, 128, "bf16", seed=N + Hkv, kv_heads=Hkv, with_do=False)
