@@ -64,7 +64,7 @@ def _check(out, ref, heads=None, groups=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [63, 200])
+@pytest.mark.parametrize("N", [1, 63, 129, 200])
 @pytest.mark.parametrize("Hkv", [1, 2, 4, 8])
 def test_gqa_ragged(lib, Hkv, N, d, causal):
     print(f"[case] gqa H=8 Hkv={Hkv} N={N} d={d} causal={causal}", flush=True)
