@@ -2,23 +2,30 @@
 """Benchmark: fused exact attention forward + backward on one MI355X.
 
 One step is one full pass of the hot path over the workload: the forward
-(attn_fwd) followed by the whole backward (the D pre-pass, the key-tile pass
-for dK/dV and the query-tile pass for dQ: the three stages attn_bwd runs).
-Inputs are seeded synthetic tensors already resident in HBM before the timed
-region.
+(attn_fwd) followed by the whole backward as attn_bwd runs it (the query-tile
+pass for dQ, which also forms D = rowsum(dO o O), then the key-tile pass for
+dK/dV).  Inputs are seeded synthetic tensors already resident in HBM before
+the timed region.
 
 Workload (default): causal self-attention, B=4, H=32, N=4096, d=128, bf16,
 scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) rounded to bf16, seed 0.  With grouped
-key/value heads (H_kv < H) the step is attn_fwd_gqa + attn_bwd_gqa and the
-backward is timed as one call (its three kernels are not split by events).
+key/value heads (H_kv < H) or a window / block list the step is the
+forward entry point + one backward call (its kernels are not split by
+events).
 
 FLOP accounting: forward 4*B*H*N^2*d, halved under the causal mask; backward
 2.5x the forward (five N^2*d products, the recompute of S included).  The
-backward runs as three kernels: the D pre-pass (HBM-bound), the key-tile pass
-for dK/dV (four N^2*d products: S, dP, dV, dK; 2.0x the forward) and the
-query-tile pass for dQ (three: S, dP, dQ; 1.5x the forward).  Per-kernel
+key-tile pass executes four N^2*d products (S, dP, dV, dK; 2.0x the forward)
+and the query-tile pass three (S, dP, dQ; 1.5x the forward).  Per-kernel
 rates below use the products each kernel executes; the backward TFLOP/s
-uses the method's 2.5x.
+uses the method's 2.5x.  Byte accounting: each kernel's algorithmic HBM
+bytes (every input it needs read once, every output written once).  The
+roofline object takes the bound from the dominant kernel's arithmetic
+intensity against the machine balance (2516.6 TFLOP/s / 8 TB/s): below it the
+kernel is HBM-bound and reported in GB/s.
+
+Other workloads: the D pre-pass alone (attn_bwd_preprocess, HBM-bound),
+decoding against a KV cache (HBM-bound) and the FP8 forward.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -45,6 +52,9 @@ WORKLOADS = {
     "causal_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128, causal=True, sigma_qk=1.0),
     "causal_b1_h16_n16384_d128": dict(B=1, H=16, N=16384, d=128, causal=True, sigma_qk=1.5),
     "noncausal_b8_h16_n2048_d64": dict(B=8, H=16, N=2048, d=64, causal=False, sigma_qk=1.0),
+    # short sequences: N = 512, d = 64, 32768 tokens per batch as in the 16-head N4096 B8 comparison;
+    # the forward's arithmetic intensity (N / 2 FLOP per byte) is below the machine balance
+    "noncausal_b64_h16_n512_d64": dict(B=64, H=16, N=512, d=64, causal=False, sigma_qk=1.0),
     # grouped key/value heads: 32 query heads share 8 K/V heads (groups of 4)
     "gqa_causal_b4_h32_hkv8_n4096_d128": dict(B=4, H=32, Hkv=8, N=4096, d=128, causal=True, sigma_qk=1.0),
     # causal sliding window of 4096 keys (window (4095, 0)) over 16384 tokens
@@ -60,6 +70,10 @@ FP8_WORKLOADS = {
     "fp8_causal_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128, causal=True),
 }
 PEAK_FP8_TFLOPS = 5033.2    # 2 x the bf16 dense peak
+# the backward's D pre-pass alone (attn_bwd_preprocess) on the benchmark shape's O and dO
+PREP_WORKLOADS = {
+    "prep_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128),
+}
 # decoding: one new token per sequence against a 32768-token KV cache
 DECODE_WORKLOADS = {
     "decode_b8_h32_hkv8_n32768_d128": dict(B=8, H=32, Hkv=8, N=32768, d=128),
@@ -138,21 +152,27 @@ def oracle_mask(cfg):
     return {}
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_causal_b4_h32_n4096_d128.json")
+MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)   # FLOP per byte
 KERNEL_KEYS = {"fwd_stag_kernel (attn_fwd)": "fwd_stag_kernel",
                "bwd_dkdv_kernel (attn_bwd_dkdv)": "bwd_dkdv_kernel",
-               "bwd_dq_kernel (attn_bwd_dq_preprocess)": "bwd_dq_kernel"}
+               "bwd_dq_kernel (attn_bwd_dq_preprocess)": "bwd_dq_kernel",
+               "bwd_prep_kernel (attn_bwd_preprocess)": "bwd_prep_kernel"}
+
+
+def traffic_record(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
 def measured_traffic(kernel_label, workload):
     """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record (already divided by the copy calibration), or None when
-    the record is for another workload or the kernel source has changed since
-    the counters were taken."""
+    WRITE_SIZE record of this workload (already divided by the copy
+    calibration), or None when there is no record for the workload or the
+    kernel source has changed since the counters were taken."""
     import hashlib
-    if workload != DEFAULT or not os.path.exists(TRAFFIC_RECORD):
+    path = traffic_record(workload)
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_RECORD))
+    rec = json.load(open(path))
     k = rec.get("kernels", {}).get(KERNEL_KEYS.get(kernel_label, ""))
     if not k:
         return None
@@ -162,6 +182,39 @@ def measured_traffic(kernel_label, workload):
     if h.hexdigest() != k["source_sha256"]:
         return None
     return int(k["hbm_read_bytes"] + k["hbm_write_bytes"])
+
+
+def kernel_bytes(B, H, Hkv, N, d):
+    """Algorithmic HBM bytes of each kernel of a bf16 step: every tensor the
+    kernel needs read once and every tensor it produces written once (bf16
+    Q, K, V, O, dO and gradients; fp32 LSE and D)."""
+    eq, ekv, rows = B * H * N * d * 2, B * Hkv * N * d * 2, B * H * N * 4
+    return {
+        "fwd": eq + 2 * ekv + eq + rows,                        # Q, K, V -> O, LSE
+        "dq": 3 * eq + 2 * ekv + rows + eq + rows,              # Q, O, dO, K, V, LSE -> dQ, D
+        "dkdv": 2 * eq + 2 * ekv + 2 * rows + 2 * ekv,          # Q, dO, K, V, LSE, D -> dK, dV
+        "bwd": 3 * eq + 2 * ekv + rows + eq + 2 * ekv,          # Q, O, dO, K, V, LSE -> dQ, dK, dV
+        "prep": 2 * eq + rows,                                  # O, dO -> D
+    }
+
+
+def roofline_entry(kernel, ms, flop, nbytes, traffic):
+    """The roofline object of one kernel: HBM-bound (GB/s against 8 TB/s) when
+    its arithmetic intensity is below the machine balance, else MFMA-bound
+    (TFLOP/s against the bf16 dense peak)."""
+    intensity = flop / nbytes
+    entry = {"kernel": kernel}
+    if intensity < MACHINE_BALANCE:
+        a = nbytes / (ms * 1e-3) / 1e9
+        entry.update({"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(a / PEAK_HBM_GBPS, 4)})
+    else:
+        a = flop / (ms * 1e-3) / 1e12
+        entry.update({"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(a / PEAK_BF16_TFLOPS, 4)})
+    entry.update({"traffic": traffic, "flops_per_launch": flop, "bytes_per_launch": nbytes,
+                  "intensity_flop_per_byte": round(intensity, 1), "avg_launch_ms": round(ms, 4)})
+    return entry
 
 
 class no_gc:
@@ -290,6 +343,75 @@ def run_fp8(args, cfg):
     return 0
 
 
+def run_prep(args, cfg):
+    """The backward's D pre-pass alone: one step is one attn_bwd_preprocess
+    call, D = rowsum(dO o O) for every row.  HBM-bound: value is its
+    algorithmic bytes (O and dO read once, D written once) per second.  O
+    comes from one untimed attn_fwd over the same inputs."""
+    import torch
+    import exact_tiled_attention_09_amd as M
+    from attn_inputs import dense_inputs
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    scale = 1.0 / math.sqrt(d)
+    log(f"workload {args.workload}: generating inputs")
+    inp = dense_inputs(B, H, N, d, "bf16", seed=0)
+    q, k, v, do = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda().contiguous() for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    M.attn_fwd(q, k, v, o, lse, scale, True, stream)
+    for _ in range(args.warmup):
+        M.attn_bwd_preprocess(o, do, ws, stream)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    with no_gc():
+        t0 = time.perf_counter()
+        for e0, e1 in events:
+            e0.record(stream)
+            M.attn_bwd_preprocess(o, do, ws, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in events)
+    nbytes = kernel_bytes(B, H, H, N, d)["prep"]
+    flop = 2.0 * B * H * N * d
+    label = "bwd_prep_kernel (attn_bwd_preprocess)"
+    roofline = roofline_entry(label, ms, flop, nbytes, measured_traffic(label, args.workload))
+    result = {
+        "metric": f"D pre-pass HBM GB/s, {args.workload}, 1 MI355X",
+        "value": roofline["achieved"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"backward D pre-pass D = rowsum(dO o O), B{B} H{H} N{N} d{d} bf16 -> fp32",
+                   "B": B, "H": H, "N": N, "d": d, "bytes_per_step": nbytes},
+        "prep": {"ms": round(ms, 4), "gbps": roofline["achieved"]},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import attention as A
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        o_h = o.float().cpu().numpy()
+        t0 = time.perf_counter()
+        A.preprocess_d(o_h, inp["do"])
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+                                  "kind": "oracle", "sample": f"the whole step (all {B * H * N} rows, fp64) "
+                                                              f"in {dt:.2f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def run_decode(args, cfg):
     """Decoding against a KV cache: one step is one attn_decode call (split
     pass + merge pass) for all B sequences.  HBM-bound: value is the
@@ -362,7 +484,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT,
-                    choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS) + sorted(FP8_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS) + sorted(FP8_WORKLOADS)
+                    + sorted(PREP_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; its FETCH_SIZE / "
@@ -399,6 +522,8 @@ def main(argv=None):
         return run_decode(args, DECODE_WORKLOADS[args.workload])
     if args.workload in FP8_WORKLOADS:
         return run_fp8(args, FP8_WORKLOADS[args.workload])
+    if args.workload in PREP_WORKLOADS:
+        return run_prep(args, PREP_WORKLOADS[args.workload])
 
     cfg = WORKLOADS[args.workload]
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
@@ -509,28 +634,27 @@ def main(argv=None):
     tflops_bwd = f_bwd / (bwd_ms * 1e-3) / 1e12
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
-    elem_q = B * H * N * d
-    elem_kv = B * Hkv * N * d
-    rows = B * H * N
-    fwd_bytes = 2 * elem_q * 2 + 2 * elem_kv * 2 + rows * 4         # read Q, K, V; write O, LSE
+    by = kernel_bytes(B, H, Hkv, N, d)
+    gbps = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)  # noqa: E731
     bwd = {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
-           "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2)}
+           "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2), "gbps": gbps(by["bwd"], bwd_ms)}
     # dominant kernel for the roofline: the longest of the MFMA kernels whose
     # launches the events bracket one by one
-    kern = {"fwd_stag_kernel (attn_fwd)": (mean["fwd"], f_fwd)}
+    kern = {"fwd_stag_kernel (attn_fwd)": (mean["fwd"], f_fwd, by["fwd"])}
     if not grouped:
         tflops_dkdv = f_dkdv / (mean["bwd_dkdv"] * 1e-3) / 1e12
         tflops_dq = f_dq / (mean["bwd_dq"] * 1e-3) / 1e12
         bwd.update({"dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
+                    "dkdv_gbps": gbps(by["dkdv"], mean["bwd_dkdv"]),
                     "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2),
-                    "dq_forms_d": True})
-        kern["bwd_dkdv_kernel (attn_bwd_dkdv)"] = (mean["bwd_dkdv"], f_dkdv)
-        kern["bwd_dq_kernel (attn_bwd_dq_preprocess)"] = (mean["bwd_dq"], f_dq)
+                    "dq_gbps": gbps(by["dq"], mean["bwd_dq"]), "dq_forms_d": True})
+        kern["bwd_dkdv_kernel (attn_bwd_dkdv)"] = (mean["bwd_dkdv"], f_dkdv, by["dkdv"])
+        kern["bwd_dq_kernel (attn_bwd_dq_preprocess)"] = (mean["bwd_dq"], f_dq, by["dq"])
     else:
-        kern = {f"fwd_stag_kernel ({fwd_name})": (mean["fwd"], f_fwd)}
+        kern = {f"fwd_stag_kernel ({fwd_name})": (mean["fwd"], f_fwd, by["fwd"])}
     dom = max(kern, key=lambda k_: kern[k_][0])
-    dom_ms, dom_flops = kern[dom]
-    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    dom_ms, dom_flops, dom_bytes = kern[dom]
+    roofline = roofline_entry(dom, dom_ms, dom_flops, dom_bytes, measured_traffic(dom, args.workload))
 
     heads = f"H{H}" + (f" H_kv{Hkv}" if Hkv != H else "")
     mask_desc = ""
@@ -557,13 +681,9 @@ def main(argv=None):
                    "visible_pairs_per_head": visible_pairs(cfg) if masked else None},
         "fwd": {"ms": round(mean["fwd"], 4), "ms_median": round(med["fwd"], 4), "tflops": round(tflops_fwd, 2),
                 "pct_mfma_peak": round(100 * tflops_fwd / PEAK_BF16_TFLOPS, 2),
-                "gbps": round(fwd_bytes / (mean["fwd"] * 1e-3) / 1e9, 1)},
+                "gbps": gbps(by["fwd"], mean["fwd"])},
         "bwd": bwd,
-        "roofline": {"kernel": dom, "bound": "mfma",
-                     "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(dom, args.workload),
-                     "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -46,6 +46,7 @@ __all__ = [
     "gqa_forward",
     "gqa_backward",
     "block_table",
+    "preprocess_d",
 ]
 
 
@@ -230,6 +231,14 @@ def head_backward_sampled(q, k, v, do, scale, causal=False, key_valid=None, quer
             dv += p.T @ do[r]
             dk += scale * (ds.T @ q[r])
     return dq, dk, dv, o, lse, dvec
+
+
+def preprocess_d(o, do):
+    """D_i = rowsum(dO o O) over the last axis, in fp64 [P1 §5.2]: the backward's
+    pre-pass on its own, for any leading shape ([B, H, N, d] -> [B, H, N]).
+    ``o`` is whatever output the pre-pass is given (the GPU's bf16 O when it
+    checks the GPU pre-pass)."""
+    return np.sum(np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64), axis=-1)
 
 
 def forward(q, k, v, scale, causal=False, heads=None):

@@ -1,6 +1,8 @@
 """Host-side logic of bench.py, CPU only: the FLOP accounting of the masked
 workloads counts exactly the (query, key) pairs the oracle's mask keeps, and
 the block patterns are valid CSR lists."""
+import math
+
 import numpy as np
 import pytest
 
@@ -48,3 +50,31 @@ def test_bench_workloads_are_well_formed():
             assert cfg["H"] % cfg["Hkv"] == 0
     assert bench.DEFAULT in bench.WORKLOADS
     assert set(bench.DECODE_WORKLOADS).isdisjoint(bench.WORKLOADS)
+
+
+def test_byte_accounting_and_roofline_bound():
+    """Algorithmic bytes per kernel, and the bound taken from arithmetic
+    intensity: the benchmark shape's kernels are MFMA-bound, the D pre-pass
+    and the short-sequence forward are HBM-bound."""
+    by = bench.kernel_bytes(4, 32, 32, 4096, 128)
+    e, r = 4 * 32 * 4096 * 128 * 2, 4 * 32 * 4096 * 4
+    assert by["fwd"] == 4 * e + r and by["prep"] == 2 * e + r
+    assert by["dq"] == 6 * e + 2 * r and by["dkdv"] == 6 * e + 2 * r and by["bwd"] == 8 * e + r
+    g = bench.kernel_bytes(1, 8, 2, 100, 64)                  # grouped heads read 1/4 of the K/V bytes
+    assert g["fwd"] == 2 * (8 * 100 * 64 * 2) + 2 * (2 * 100 * 64 * 2) + 8 * 100 * 4
+    f, _ = bench.flops(4, 32, 4096, 128, True)
+    big = bench.roofline_entry("k", 1.0, 2.0 * f, by["dkdv"], None)
+    assert big["bound"] == "mfma" and big["unit"] == "TFLOP/s"
+    assert math.isclose(big["achieved"], round(2.0 * f / 1e-3 / 1e12, 2))
+    prep = bench.roofline_entry("p", 0.05, 2.0 * 4 * 32 * 4096 * 128, by["prep"], None)
+    assert prep["bound"] == "hbm" and prep["unit"] == "GB/s" and prep["peak"] == bench.PEAK_HBM_GBPS
+    assert math.isclose(prep["achieved"], round(by["prep"] / 0.05e-3 / 1e9, 1))
+    c = bench.WORKLOADS["noncausal_b64_h16_n512_d64"]
+    fs, _ = bench.flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+    fb = bench.kernel_bytes(c["B"], c["H"], c["H"], c["N"], c["d"])["fwd"]
+    assert fs / fb < bench.MACHINE_BALANCE
+
+
+def test_every_workload_name_is_unique():
+    names = [*bench.WORKLOADS, *bench.DECODE_WORKLOADS, *bench.FP8_WORKLOADS, *bench.PREP_WORKLOADS]
+    assert len(names) == len(set(names))

@@ -104,6 +104,49 @@ def test_config3_fwd_bwd_causal_d128(lib):
     _check_heads(out, inp, scale, True, [(0, 0), (2, 17), (3, 31)], bwd=True)
 
 
+def test_short_sequences_noncausal_d64(lib):
+    """B=64, H=16, N=512, d=64, bf16 forward and backward, non-causal: the
+    short-sequence shape the benchmark times (two 256-row query tiles per
+    head, 32768 tokens in all)."""
+    _say("short sequences: generate")
+    inp = dense_inputs(64, 16, 512, 64, "bf16", seed=0)
+    out = _dense_run(lib, inp, 1 / 8, False, bwd=True)
+    _all_heads_properties(out, inp, 1 / 8, False)
+    _check_heads(out, inp, 1 / 8, False, [(0, 0), (31, 7), (63, 15)], bwd=True)
+
+
+def test_d_prepass_benchmark_shape(lib):
+    """The backward's D pre-pass (attn_bwd_preprocess) at B=4, H=32, N=4096,
+    d=128, on the forward's own bf16 O: every row of D against the oracle's
+    rowsum(dO o O) in fp64.  The bound is fp32 summation of 128 products,
+    1e-5 of sum |dO o O| per row.  The dQ pass's D (attn_bwd_dq_preprocess)
+    must be the same bits."""
+    import torch
+    _say("D pre-pass: generate")
+    B, H, N, d = 4, 32, 4096, 128
+    inp = dense_inputs(B, H, N, d, "bf16", seed=0)
+    q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    scale = 1 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    lib.attn_fwd(q, k, v, o, lse, scale, True)
+    ws = torch.empty(lib.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    lib.attn_bwd_preprocess(o, do, ws)
+    torch.cuda.synchronize()
+    d_gpu = ws[: B * H * N * 4].view(torch.float32).view(B, H, N).clone()
+    o_h = to_np(o)
+    ref = A.preprocess_d(o_h, inp["do"])
+    bound = 1e-5 * A.preprocess_d(np.abs(o_h), np.abs(inp["do"])) + 1e-30
+    err = np.abs(to_np(d_gpu) - ref)
+    _say(f"  D: max abs err {err.max():.2e}, max err / bound {np.max(err / bound):.3f}")
+    assert np.all(err <= bound)
+    ws.zero_()
+    dq = torch.empty_like(q)
+    lib.attn_bwd_dq_preprocess(q, k, v, o, lse, do, dq, scale, True, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ws[: B * H * N * 4].view(torch.float32).view(B, H, N), d_gpu)
+
+
 def test_config4_long_sequence_sharp_scores(lib):
     """B=1, H=16, N=16384, d=128, causal, Q and K ~ N(0, 1.5^2): the running
     max moves often.  Head 0 is checked whole; head 15 at sampled query rows

@@ -388,3 +388,27 @@ def test_sampled_backward_matches_full_backward(causal):
     np.testing.assert_allclose(sk, dk[cols], atol=1e-13)
     np.testing.assert_allclose(sv_, dv[cols], atol=1e-13)
     np.testing.assert_allclose(so, o, atol=1e-14)
+
+
+def test_preprocess_d_pins():
+    """The pre-pass alone: D = rowsum(dO o O) [P1 §5.2].  Pinned to the other
+    form of the same quantity, rowsum(P o dP), which head_backward checks
+    against its own D, and to one-hot rows of O, where D picks one entry of
+    dO (a sum over the wrong axis or a dropped factor fails either)."""
+    rng = np.random.default_rng(13)
+    n, d = 23, 5
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    *_, o, _, dvec = A.head_backward(q, k, v, g, 0.5, True)
+    np.testing.assert_allclose(A.preprocess_d(o, g), dvec, atol=1e-13)
+    s = 0.5 * q @ k.T
+    s[np.triu_indices(n, 1)] = -np.inf
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(A.preprocess_d(o, g), np.sum(p * (g @ v.T), axis=1), atol=1e-12)
+    one_hot = np.zeros((2, 3, n, d))
+    idx = rng.integers(0, d, size=(2, 3, n))
+    np.put_along_axis(one_hot, idx[..., None], 1.0, axis=-1)
+    dO = rng.standard_normal((2, 3, n, d))
+    dd = A.preprocess_d(one_hot, dO)
+    assert dd.shape == (2, 3, n)
+    np.testing.assert_array_equal(dd, np.take_along_axis(dO, idx[..., None], axis=-1)[..., 0])
