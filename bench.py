@@ -364,16 +364,18 @@ def run_prep(args, cfg):
     for _ in range(args.warmup):
         M.attn_bwd_preprocess(o, do, ws, stream)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # one event pair around the back-to-back launches: for a ~40 us kernel a
+    # pair around every launch would add its own few microseconds
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with no_gc():
         t0 = time.perf_counter()
-        for e0, e1 in events:
-            e0.record(stream)
+        e0.record(stream)
+        for _ in range(args.steps):
             M.attn_bwd_preprocess(o, do, ws, stream)
-            e1.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    ms = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in events)
+    ms = e0.elapsed_time(e1) / args.steps
     nbytes = kernel_bytes(B, H, H, N, d)["prep"]
     flop = 2.0 * B * H * N * d
     label = "bwd_prep_kernel (attn_bwd_preprocess)"
