@@ -343,7 +343,10 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   __shared__ uint32_t s_anypad[4];
 
   int bh, tile;
-  wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);  // causal: heaviest first
+  // causal: groups of two heads per XCD, heaviest tiles first in each group;
+  // otherwise tile-major (measured faster than one head at a time at N = 512)
+  if (CAUSAL) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 2, true, bh, tile);
+  else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const SeqView sv = seq_view<VARLEN>(a, b, h, D);
