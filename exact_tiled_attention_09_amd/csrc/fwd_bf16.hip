@@ -27,9 +27,9 @@
 //    the same O = O~ / l and LSE = m + log2 l, so this changes only rounding.
 //  * causal: key tiles above the diagonal are never loaded; only tiles that
 //    cross the diagonal, the sequence end or a padded key are masked
-//    element-wise; query tiles are issued heaviest first; consecutive
-//    workgroups of one (sequence, head) are spread so that the 8 XCDs each
-//    keep whole heads in their L2 when B*H is a multiple of 8.
+//    element-wise; in the default (staggered) form each XCD takes its heads
+//    four at a time, their query tiles heaviest first (wg_coords_grouped);
+//    without a causal mask all heads' tile 0 go first, then all tile 1, ...
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
@@ -343,9 +343,9 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   __shared__ uint32_t s_anypad[4];
 
   int bh, tile;
-  // causal: groups of two heads per XCD, heaviest tiles first in each group;
+  // causal: groups of four heads per XCD, heaviest tiles first in each group;
   // otherwise tile-major (measured faster than one head at a time at N = 512)
-  if (CAUSAL) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 2, true, bh, tile);
+  if (CAUSAL) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, true, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;

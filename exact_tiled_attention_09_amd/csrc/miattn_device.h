@@ -234,8 +234,8 @@ __device__ __forceinline__ void wg_coords(int w, int nbh, int ntile, bool heavy_
 // per XCD while the heavy tiles of a group still start before its light ones
 // (under a causal mask one head at a time would leave the heaviest tile of
 // the last head to start late: about 9% longer in a greedy-schedule model of
-// 16 heads x 16 tiles on 32 CUs, against none for groups of two).  The result
-// is a bijection of [0, nbh*ntile).
+// 16 heads x 16 tiles on 32 CUs, against none for groups of two or more).
+// The result is a bijection of [0, nbh*ntile).
 __host__ __device__ __forceinline__ void wg_coords_grouped(int w, int nbh, int ntile, int group,
                                                            bool heavy_last_tile, int& bh, int& t) {
   const int total = nbh * ntile;
