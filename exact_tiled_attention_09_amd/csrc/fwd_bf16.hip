@@ -343,9 +343,10 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   __shared__ uint32_t s_anypad[4];
 
   int bh, tile;
-  // causal: groups of four heads per XCD, heaviest tiles first in each group;
-  // otherwise tile-major (measured faster than one head at a time at N = 512)
-  if (CAUSAL) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, true, bh, tile);
+  // causal masks, windows and block lists: groups of four heads per XCD,
+  // heaviest tiles first in each group under a causal mask; plain non-causal:
+  // all heads' tile 0, then all tile 1, ... (measured faster there)
+  if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
