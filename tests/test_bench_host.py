@@ -78,3 +78,12 @@ def test_byte_accounting_and_roofline_bound():
 def test_every_workload_name_is_unique():
     names = [*bench.WORKLOADS, *bench.DECODE_WORKLOADS, *bench.FP8_WORKLOADS, *bench.PREP_WORKLOADS]
     assert len(names) == len(set(names))
+
+
+def test_cli_refuses_several_gpus_and_bad_counts(capsys):
+    """One GPU only: --gpus above 1 ends with a message and status 2 before
+    anything touches a device; so do non-positive step counts."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().err
+    assert bench.main(["--steps", "0"]) == 2
+    assert bench.main(["--warmup", "-1"]) == 2
