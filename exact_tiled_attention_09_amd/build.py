@@ -43,9 +43,6 @@ COMMON_FLAGS = [
 # between register files every iteration, the VGPR form does not.
 FILE_FLAGS = {
     "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    # the four-wave forward keeps O in AGPRs through inline MFMAs only; all
-    # compiler-generated MFMAs stay in VGPR form
-    "fwd_w4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

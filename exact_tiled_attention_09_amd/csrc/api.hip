@@ -2,7 +2,6 @@
 // dispatch to the gfx950 kernels.  Nothing here allocates, frees or
 // synchronises; every launch goes to the caller's stream.
 #include <cmath>
-#include <cstdlib>
 #include <cstdint>
 
 #include "../../include/miattn.h"
@@ -93,19 +92,11 @@ int sparse_args(AttnArgs& a, int N, const int* row_ptr, const int* col_idx, int 
 
 // Split plan of decoding: about one wave per SIMD of the chip (1024 waves) in
 // total, at least 256 keys per piece, pieces a multiple of 64 keys.
-// MIATTN_DECODE_WAVES overrides the wave target for tuning sweeps.
-int64_t decode_wave_target() {
-  static const int64_t target = [] {
-    const char* e = getenv("MIATTN_DECODE_WAVES");
-    const long v = e ? atol(e) : 0;
-    return (int64_t)(v >= 64 && v <= (1 << 20) ? v : 1024);
-  }();
-  return target;
-}
+constexpr int64_t kDecodeWaveTarget = 1024;
 
 void decode_plan(int B, int H, int H_kv, int N, int* nsplit, int* chunk) {
   const int64_t units = (int64_t)B * H_kv * ((H / H_kv + 31) / 32);
-  const int64_t want = (decode_wave_target() + units - 1) / units;
+  const int64_t want = (kDecodeWaveTarget + units - 1) / units;
   const int64_t most = ((int64_t)N + 255) / 256;
   int64_t ns = want < most ? want : most;
   if (ns < 1) ns = 1;

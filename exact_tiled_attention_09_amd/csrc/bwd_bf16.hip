@@ -30,7 +30,6 @@
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
-#include <cstdlib>
 #include <type_traits>
 
 namespace miattn {
@@ -833,16 +832,9 @@ hipError_t launch_bwd_prep_bf16(const AttnArgs& a, int d, bool varlen, hipStream
 // Waves per dK/dV workgroup for the plain layouts.  d = 128: eight (two per
 // SIMD), 10-13% faster than four.  d = 64: four (one per SIMD, handling both
 // query halves of a step), 6% faster at N = 2048 and 16% at N = 512, where
-// the eight-wave form's per-step overheads weigh most.  MIATTN_DKDV_WAVES=4
-// or 8 forces one form for tuning sweeps.
-static int dkdv_waves(int d) {
-  static int forced = [] {
-    const char* e = getenv("MIATTN_DKDV_WAVES");
-    const int v = e ? atoi(e) : 0;
-    return (v == 4 || v == 8) ? v : 0;
-  }();
-  return forced ? forced : (d == 64 ? 4 : 8);
-}
+// the eight-wave form's per-step overheads weigh most.  Windows and block
+// lists always take eight.
+constexpr int dkdv_waves(int d) { return d == 64 ? 4 : 8; }
 
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 static hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {

@@ -6,9 +6,9 @@
 // 累计梯度", section 01).  The N x N scores never leave registers.
 //
 // Work decomposition (MI355X-first, not the pages' thread-block layout):
-//  * one workgroup per (sequence, head, query tile of BR = NW * QB * 32 rows);
-//    each wave owns QB blocks of 32 query rows ("split-Q": no cross-wave
-//    softmax traffic).
+//  * one workgroup per (sequence, head, query tile of 256 rows); each of its
+//    eight waves owns 32 query rows ("split-Q": no cross-wave softmax
+//    traffic).
 //  * the wave computes S^T = K Q^T so that the 32x32 accumulator puts one query
 //    per lane column: row max / row sum are in-lane over 16 registers plus one
 //    exchange with the lane 32 away, and the rescale factor is a per-lane
@@ -16,8 +16,8 @@
 //  * P^T leaves the accumulator already in the B-operand layout of
 //    O^T += V^T P^T; V^T comes from the row-major V tile through the LDS
 //    transpose read, so neither P nor V is shuffled.
-//  * K/V tiles of BC = 64 keys are double-buffered in LDS (one barrier per
-//    tile) in the XOR-swizzled layout of swz<D>, which keeps both the b128
+//  * K/V tiles of BC = 64 keys go through three LDS buffers each (one barrier
+//    per tile) in the XOR-swizzled layout of swz<D>, which keeps both the b128
 //    operand reads and the transpose reads free of bank conflicts; Q stays in
 //    registers for the whole key loop.
 //  * softmax runs in base 2 with scale * log2(e) folded into one FMA.  A row's
@@ -27,288 +27,16 @@
 //    the same O = O~ / l and LSE = m + log2 l, so this changes only rounding.
 //  * causal: key tiles above the diagonal are never loaded; only tiles that
 //    cross the diagonal, the sequence end or a padded key are masked
-//    element-wise; in the default (staggered) form each XCD takes its heads
-//    four at a time, their query tiles heaviest first (wg_coords_grouped);
+//    element-wise; each XCD takes its heads four at a time, their query tiles heaviest first (wg_coords_grouped);
 //    without a causal mask all heads' tile 0 go first, then all tile 1, ...
 #include "miattn_device.h"
 #include "miattn_launch.h"
 
-#include <cstdlib>
 #include <type_traits>
 
 namespace miattn {
 
-template <int D, int QB, int NW, int MINB, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
-  constexpr int BC = 64;                 // keys per tile
-  constexpr int BR = NW * QB * 32;       // query rows per workgroup
-  constexpr int KS = D / 16;             // k-steps of S over the head dim
-  constexpr int DB = D / 32;             // 32-wide blocks of O columns
-  constexpr int TILE = BC * D;           // one K or V tile (swizzled rows, see swz)
-  constexpr int NT = NW * 64;
-  constexpr int CH_PER_ROW = D / 8;      // 16-byte chunks per row
-  constexpr int CPT = BC * CH_PER_ROW / NT;
-  static_assert(CPT * NT == BC * CH_PER_ROW, "tile chunks must divide evenly");
-
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
-  __shared__ uint8_t s_valid[2][BC];
-  __shared__ uint32_t s_anypad[2];
-
-  int bh, tile;
-  wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);  // causal: heaviest first
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const SeqView sv = seq_view<VARLEN>(a, b, h, D);
-  const int q_tile0 = tile * BR;
-  if (q_tile0 >= sv.len) return;  // uniform across the workgroup, before any barrier
-
-  const int tid = threadIdx.x;
-  const int wave = wave_id();
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int q_wave0 = q_tile0 + wave * QB * 32;
-
-  const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
-
-  // A negative scale is handled by flipping the sign of Q once.
-  float c = a.scale_log2;
-  const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
-  c = fabsf(c);
-
-  // Q as the B operand of S^T = K Q^T: lane (query l32, half hi) holds
-  // features ks*16 + hi*8 .. +7 for every k-step ks.
-  bf16x8 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = q_wave0 + qb * 32 + l32;
-    const bool ok = qi < sv.len;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok) x = *(const u32x4*)(qp + (int64_t)qi * sv.tok_stride + ks * 16 + hi * 8);
-      x ^= qsign;
-      qf[qb][ks] = as_bf16x8(x);
-    }
-  }
-
-  f32x16 o[QB][DB];
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = kNegInf;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
-  }
-
-  const int kv_len = sv.len;
-  const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
-  const int ntiles = (kv_end + BC - 1) / BC;
-
-  u32x4 rk[CPT], rv[CPT];
-  uint32_t rvalid = 1u;
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int cidx = 0; cidx < CPT; ++cidx) {
-      const int chunk = tid + cidx * NT;
-      const int row = chunk / CH_PER_ROW;
-      const int col = (chunk - row * CH_PER_ROW) * 8;
-      const int key = j * BC + row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < kv_len) {
-        zk = *(const u32x4*)(kp + (int64_t)key * sv.kv_stride + col);
-        zv = *(const u32x4*)(vp + (int64_t)key * sv.kv_stride + col);
-      }
-      rk[cidx] = zk;
-      rv[cidx] = zv;
-    }
-    if constexpr (KPAD) {
-      if (wave == 0) {
-        const int key = j * BC + lane;
-        rvalid = (key < kv_len) ? (uint32_t)(a.key_valid[sv.tok0 + key] != 0) : 1u;
-      }
-    }
-  };
-  int st_off[CPT];  // swizzled LDS offset of each staged chunk
-#pragma unroll
-  for (int cidx = 0; cidx < CPT; ++cidx) {
-    const int chunk = tid + cidx * NT;
-    const int row = chunk / CH_PER_ROW;
-    st_off[cidx] = swz_off<D>(row, (chunk - row * CH_PER_ROW) * 8);
-  }
-  auto store_tile = [&](int buf) {
-    uint16_t* sk = smem + buf * 2 * TILE;
-    uint16_t* sv_ = sk + TILE;
-#pragma unroll
-    for (int cidx = 0; cidx < CPT; ++cidx) {
-      *(u32x4*)(sk + st_off[cidx]) = rk[cidx];
-      *(u32x4*)(sv_ + st_off[cidx]) = rv[cidx];
-    }
-    if constexpr (KPAD) {
-      if (wave == 0) {
-        s_valid[buf][lane] = (uint8_t)rvalid;
-        const bool any = wave_any(rvalid == 0u);
-        if (lane == 0) s_anypad[buf] = any ? 1u : 0u;
-      }
-    }
-  };
-
-  // Per-lane operand offsets inside a tile (the swizzle of a row depends only
-  // on the row modulo 16, so 32-row and 16-row steps reuse them).
-  int koff[KS];       // K as the A operand of S^T: row kb*32 + l32, chunk 2*ks + hi
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
-  const int tr_r = hi * 4 + ((lane >> 2) & 3);
-  const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  int voff[2][DB];    // V through the transpose read: rows 8R + tr_r, columns db*32 + tr_c
-#pragma unroll
-  for (int R = 0; R < 2; ++R)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) voff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-
-    const int kt0 = j * BC;
-    const bool wave_live = !CAUSAL || kt0 <= q_wave0 + QB * 32 - 1;
-    if (wave_live) {
-      const uint16_t* sk = smem + buf * 2 * TILE;
-      const uint16_t* svt = sk + TILE;
-
-      // S^T = K Q^T for two 32-key blocks.
-      f32x16 s[2][QB];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16(ka, qf[qb][ks], s[kb][qb]);
-        }
-      }
-
-      bool need_mask = kt0 + BC > kv_len;
-      if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
-      if (KPAD) need_mask = need_mask || (s_anypad[buf] != 0u);
-      float cc = c;
-      if (need_mask) {
-        // Scale first, then hide masked entries as -inf; afterwards the
-        // exponent uses multiplier 1 (so scale == 0 cannot make 0 * -inf).
-        cc = 1.f;
-        const int q_lane = pin_in_branch(q_wave0 + l32);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int qi = q_lane + qb * 32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-              const int key = kt0 + kl;
-              bool vis = key < kv_len;
-              if (CAUSAL) vis = vis && key <= qi;
-              if (KPAD) vis = vis && s_valid[buf][kl] != 0;
-              s[kb][qb][r] = vis ? s[kb][qb][r] * c : kNegInf;
-            }
-          }
-      }
-
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = wave_max_halves(mx);
-        const float mt = need_mask ? mx : mx * c;
-        const float m_new = (mt > m[qb] + kLazyMax) ? mt : m[qb];
-        const bool dead = m_new == kNegInf;  // no visible key yet for this row
-        const float alpha = dead ? 1.f : fast_exp2(m[qb] - m_new);
-        const float mu = dead ? 0.f : m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(__builtin_fmaf(s[kb][qb][r], cc, -mu));
-            rs += p;
-            s[kb][qb][r] = p;
-          }
-        l[qb] = alpha * l[qb] + rs;
-        m[qb] = m_new;
-        if (wave_any(alpha != 1.f)) {
-          const float a_ = pin_in_branch(alpha);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[qb][db] *= a_;
-        }
-      }
-
-      // O^T += V^T P^T, 16 keys per MFMA.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 pb[QB];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const f32x16& x = s[kb][qb];
-            pb[qb] = pack_bf16x8(x[8 * t + 0], x[8 * t + 1], x[8 * t + 2], x[8 * t + 3],
-                                 x[8 * t + 4], x[8 * t + 5], x[8 * t + 6], x[8 * t + 7]);
-          }
-          const uint16_t* vt = svt + (kb * 32 + 16 * t) * D;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 va = join_u32x2(lds_read_tr16(vt + voff[0][db]), lds_read_tr16(vt + voff[1][db]));
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma_bf16(va, pb[qb], o[qb][db]);
-          }
-        }
-    }
-
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: O = O~ / l, LSE = ln 2 * (m + log2 l); a row that saw no
-  // visible key gets O = 0 and LSE = -inf.
-  uint16_t* __restrict__ op = (uint16_t*)a.o + sv.base;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = wave_sum_halves(l[qb]);
-    const int qi = q_wave0 + qb * 32 + l32;
-    if (qi < sv.len) {
-      const bool dead = (m[qb] == kNegInf) || !(lt > 0.f);
-      const float inv = dead ? 0.f : 1.f / lt;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& x = o[qb][db];
-          u32x2 w = {pack_bf16x2(x[4 * g + 0] * inv, x[4 * g + 1] * inv),
-                     pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-          *(u32x2*)(op + (int64_t)qi * sv.tok_stride + db * 32 + g * 8 + hi * 4) = w;
-        }
-      if (hi == 0) a.lse[sv.row_base + qi] = dead ? kNegInf : (m[qb] + fast_log2(lt)) * kLn2;
-    }
-  }
-}
-
-// Staggered form with direct loads (the default).  Eight waves of 32 query
+// Staggered schedule with direct loads.  Eight waves of 32 query
 // rows, two per SIMD, one barrier per interval.  Every wave runs, for each key tile j,
 //   S_j^T = K_j Q^T (MFMA),  softmax of S_j (VALU),  O^T += V_j^T P_j^T (MFMA),
 // and interval j ends after S_j for late waves and after softmax_j for early
@@ -320,11 +48,10 @@ __global__ void __launch_bounds__(NW * 64, MINB) fwd_bf16_kernel(AttnArgs a, int
 // being fetched during interval t, and before the barrier that ends interval
 // t each wave waits only for its own loads of K_{t+1} and V_t.  Key-validity
 // flags of tile t are read as late as interval t+1 and written two intervals
-// ahead, so they are kept four deep.  ROLE picks the late waves: 0 = waves
-// 4-7 (the partner of wave w on its SIMD is w + 4), 1 = odd waves.  The loop
-// is unrolled by the three buffers so that every LDS address is a register
+// ahead, so they are kept four deep.  The late waves are 4-7 (the partner of
+// wave w on its SIMD is w + 4).  The loop is unrolled by the three buffers so that every LDS address is a register
 // plus an immediate.
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE, int MASK = kMaskPlain>
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtiles) {
   constexpr int NW = 8;
   constexpr int BC = 64;
@@ -359,7 +86,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const bool late = ROLE == 0 ? (wave >= 4) : ((wave & 1) != 0);
+  const bool late = wave >= 4;  // the partner of wave w on its SIMD is w + 4
   const int q_wave0 = q_tile0 + wave * 32;
   const int kv_len = sv.len;
 
@@ -657,7 +384,9 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   const float lt = wave_sum_halves(l);
   const int qi = q_wave0 + l32;
   if (qi < sv.len) {
-    const bool dead = (m == kNegInf) || !(lt > 0.f);
+    // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
+    // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
+    const bool dead = (m == kNegInf) && !(lt != lt);
     const float inv = dead ? 0.f : 1.f / lt;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -672,418 +401,34 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   }
 }
 
-// Direct-load form.  Same per-wave work as fwd_bf16_kernel
-// with one 32-row block per wave, but K and V tiles travel from global memory
-// straight into LDS (global_load_lds_dwordx4: no register staging and no LDS
-// stores) NBUF - 1 tiles ahead, through NBUF buffers per tensor.  Before the
-// barrier that ends tile j, each wave waits only for its own loads of tile
-// j+1, so a load has NBUF - 1 tiles of compute to land.  The key loop is
-// unrolled by NBUF so that every buffer address is a compile-time constant.
-// Rows past the end of the sequence are loaded from its last row (finite
-// values) and masked.  NW = 8 runs one workgroup of 256 rows per CU; NW = 4
-// with two buffers runs two independent workgroups of 128 rows per CU, each
-// with its own barrier, so the two waves that share a SIMD are not held in
-// step by a common barrier.
-template <int D, int NW, int NBUF, bool CAUSAL, bool VARLEN, bool KPAD>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_dma_kernel(AttnArgs a, int n_qtiles) {
-  constexpr int BC = 64;
-  constexpr int BR = NW * 32;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int TILE = BC * D;
-  constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int LPT = BC * CPR / NT;     // direct loads per thread per tensor and tile
-  constexpr int AHEAD = NBUF - 1;        // tiles in flight ahead of the one in use
-  static_assert(LPT * NT == BC * CPR, "tile chunks must divide evenly");
-  static_assert(NBUF >= 2 && NBUF <= 4, "two to four buffers");
-  static_assert(AHEAD * 2 * LPT < 64, "vmcnt field of 6 bits");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
-  __shared__ uint8_t s_valid[NBUF][BC];
-  __shared__ uint32_t s_anypad[NBUF];
-
-  int bh, tile;
-  wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);  // causal: heaviest first
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const SeqView sv = seq_view<VARLEN>(a, b, h, D);
-  const int q_tile0 = tile * BR;
-  if (q_tile0 >= sv.len) return;  // uniform across the workgroup, before any barrier
-
-  const int tid = threadIdx.x;
-  const int wave = wave_id();
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int q_wave0 = q_tile0 + wave * 32;
-  const int kv_len = sv.len;
-
-  const uint16_t* __restrict__ qp = (const uint16_t*)a.q + sv.base;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k + sv.kv_base;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v + sv.kv_base;
-
-  float c = a.scale_log2;
-  const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
-  c = fabsf(c);
-
-  bf16x8 qf[KS];  // loaded in the prologue
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = kNegInf, l = 0.f;
-
-  const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
-  const int ntiles = (kv_end + BC - 1) / BC;
-
-  // Direct-load sources: LDS chunk p = i*NT + tid of a tile holds row p / CPR,
-  // logical chunk (p % CPR) ^ swz(row).
-  int src_row[LPT], src_col[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int pch = i * NT + tid;
-    const int row = pch / CPR;
-    src_row[i] = row;
-    src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
-  }
-  // Load number n (0 .. 2*LPT-1) of this thread for tile j: K for even n, V
-  // for odd n, chunk n / 2.
-  auto issue_part = [&](int j, int n) {
-    const int i = n >> 1;
-    const int key = min(j * BC + src_row[i], kv_len - 1);
-    const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
-    if (n & 1) lds_dma16(vp + off, sV[j % NBUF] + (i * NT + wave * 64) * 8);
-    else lds_dma16(kp + off, sK[j % NBUF] + (i * NT + wave * 64) * 8);
-  };
-  auto issue = [&](int j) {
-#pragma unroll
-    for (int n = 0; n < 2 * LPT; ++n) issue_part(j, n);
-  };
-  // Key-validity flags of a tile, by wave 0: the raw byte is loaded before
-  // the tile's direct loads are issued and converted only when stored at the
-  // end of the step, so the wave does not wait in between.
-  uint32_t rvalid = 1u;
-  int rkey = 0;
-  auto load_flags = [&](int j) {
-    if constexpr (KPAD) {
-      if (wave == 0) {
-        rkey = j * BC + lane;
-        rvalid = a.key_valid[sv.tok0 + min(rkey, kv_len - 1)];
-      }
-    }
-  };
-  auto store_flags = [&](int slot) {
-    if constexpr (KPAD) {
-      if (wave == 0) {
-        const uint32_t ok = (rkey >= kv_len || rvalid != 0u) ? 1u : 0u;  // keys past the end are masked anyway
-        s_valid[slot][lane] = (uint8_t)ok;
-        const bool any = wave_any(ok == 0u);
-        if (lane == 0) s_anypad[slot] = any ? 1u : 0u;
-      }
-    }
-  };
-
-  int koff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = swz_off<D>(l32, ks * 16 + hi * 8);
-  const int tr_r = hi * 4 + ((lane >> 2) & 3);
-  const int tr_c = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  int voff[2][DB];
-#pragma unroll
-  for (int R = 0; R < 2; ++R)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) voff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
-
-  // One key tile from buffer slot U (= j % NBUF): S^T = K Q^T, mask, online
-  // softmax, O^T += V^T P^T; tile j + AHEAD is fetched meanwhile.
-  auto step = [&](int j, auto slot_c) {
-    constexpr int U = decltype(slot_c)::value;
-    constexpr int NU = (U + AHEAD) % NBUF;
-    const uint16_t* sk = sK[U];
-    const uint16_t* svt = sV[U];
-    const bool fetch = j + AHEAD < ntiles;
-    const int kt0 = j * BC;
-    const bool wave_live = !CAUSAL || kt0 <= q_wave0 + 31;
-    if (fetch) load_flags(j + AHEAD);
-    // A wave with work spreads its loads of tile j+AHEAD over the S^T MFMAs
-    // (all waves issuing together would queue in the CU's memory pipeline);
-    // an idle wave issues them at once.
-    if (fetch && !wave_live) issue(j + AHEAD);
-    if (wave_live) {
-      // K operands are read two k-steps ahead of their MFMAs.
-      f32x16 s[2];
-      s[0] = f32x16{};
-      s[1] = f32x16{};
-      bf16x8 ka[3][2];
-      auto kread = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dst[kb] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
-      };
-      kread(0, ka[0]);
-      kread(1, ka[1]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(ka[ks % 3][kb], qf[ks], s[kb]);
-        if (fetch) {
-#pragma unroll
-          for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + AHEAD, n);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      bool need_mask = kt0 + BC > kv_len;
-      if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
-      if (KPAD) need_mask = need_mask || (s_anypad[U] != 0u);
-      float cc = c;
-      if (need_mask) {
-        // Scale first, then hide masked entries as -inf; afterwards the
-        // exponent uses multiplier 1 (so scale == 0 cannot make 0 * -inf).
-        cc = 1.f;
-        const int qi = pin_in_branch(q_wave0 + l32);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            const int key = kt0 + kl;
-            bool vis = key < kv_len;
-            if (CAUSAL) vis = vis && key <= qi;
-            if (KPAD) vis = vis && s_valid[U][kl] != 0;
-            s[kb][r] = vis ? s[kb][r] * c : kNegInf;
-          }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = wave_max_halves(mx) * cc;
-      const float m_new = (mx > m + kLazyMax) ? mx : m;
-      const bool dead = m_new == kNegInf;  // no visible key yet for this row
-      const float alpha = dead ? 1.f : fast_exp2(m - m_new);
-      const float mu = dead ? 0.f : m_new;
-      float rs = 0.f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e[i] = fast_exp2(__builtin_fmaf(s[kb][8 * t + i], cc, -mu));
-            rs += e[i];
-          }
-          pb[kb * 2 + t] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-        }
-      l = alpha * l + rs;
-      m = m_new;
-      if (wave_any(alpha != 1.f)) {
-        const float a_ = pin_in_branch(alpha);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= a_;
-      }
-      // O^T += V^T P^T; V operands are read three MFMAs ahead.
-      {
-        constexpr int NPV = 4 * DB;
-        constexpr int PF = 3;
-        auto vread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-          const uint16_t* v0 = svt + (i / DB) * 16 * D;  // keys 16 (i / DB) .. +15
-          return join_u32x2(lds_read_tr16(v0 + voff[0][i % DB]), lds_read_tr16(v0 + voff[1][i % DB]));
-        };
-        bf16x8 va[NPV];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) va[i] = vread(i);
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-          if (i + PF < NPV) va[i + PF] = vread(i + PF);
-          o[i % DB] = mfma_bf16(va[i], pb[i / DB], o[i % DB]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    if (fetch) store_flags(NU);
-    // this wave's loads of tile j + 1 have landed (those issued after them,
-    // for tiles j + 2 .. j + AHEAD, may not have)
-    if constexpr (AHEAD == 3) {
-      if (fetch) barrier_vmem_n<4 * LPT>();
-      else if (j + 2 < ntiles) barrier_vmem_n<2 * LPT>();
-      else barrier_vmem_n<0>();
-    } else if constexpr (AHEAD == 2) {
-      if (fetch) barrier_vmem_n<2 * LPT>();
-      else barrier_vmem_n<0>();
-    } else {
-      barrier_vmem_n<0>();
-    }
-  };
-
-  // Prologue: start tiles 0 .. AHEAD-1, then load this wave's Q rows; one
-  // wait (which the compiler sees, so the loop waits for none of these loads
-  // again) covers all of them.
-#pragma unroll
-  for (int t = 0; t < AHEAD; ++t) {
-    if (t < ntiles) {
-      load_flags(t);
-      store_flags(t);
-      issue(t);
-    }
-  }
-  {
-    // rows past the sequence load its last row and are zeroed (no branch)
-    const int qi = q_wave0 + l32;
-    const uint32_t keep = qi < kv_len ? 0xffffffffu : 0u;
-    const uint16_t* qrow = qp + (int64_t)min(qi, kv_len - 1) * sv.tok_stride + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8((*(const u32x4*)(qrow + ks * 16) & keep) ^ qsign);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  barrier_vmem_n<0>();
-  for (int j = 0; j < ntiles; j += NBUF) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
-    if constexpr (NBUF >= 3) {
-      if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
-    }
-    if constexpr (NBUF >= 4) {
-      if (j + 3 < ntiles) step(j + 3, std::integral_constant<int, 3>{});
-    }
-  }
-
-  // Epilogue: O = O~ / l, LSE = ln 2 * (m + log2 l); a row that saw no
-  // visible key gets O = 0 and LSE = -inf.
-  uint16_t* __restrict__ op = (uint16_t*)a.o + sv.base;
-  const float lt = wave_sum_halves(l);
-  const int qi = q_wave0 + l32;
-  if (qi < sv.len) {
-    const bool dead = (m == kNegInf) || !(lt > 0.f);
-    const float inv = dead ? 0.f : 1.f / lt;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& x = o[db];
-        u32x2 w = {pack_bf16x2(x[4 * g + 0] * inv, x[4 * g + 1] * inv),
-                   pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-        *(u32x2*)(op + (int64_t)qi * sv.tok_stride + db * 32 + g * 8 + hi * 4) = w;
-      }
-    if (hi == 0) a.lse[sv.row_base + qi] = dead ? kNegInf : (m + fast_log2(lt)) * kLn2;
-  }
-}
-
-template <int D, int NW, int NBUF, bool CAUSAL, bool VARLEN, bool KPAD>
-static hipError_t launch_fwd_dma_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * 32;
-  const int n_qtiles = (a.N + BR - 1) / BR;
-  const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_dma_kernel<D, NW, NBUF, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     stream, a, n_qtiles);
-  return hipGetLastError();
-}
-
-template <int D, int NW, int NBUF>
-static hipError_t dispatch_fwd_dma(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
-  if (varlen) {
-    if (causal) return kpad ? launch_fwd_dma_t<D, NW, NBUF, true, true, true>(a, s)
-                            : launch_fwd_dma_t<D, NW, NBUF, true, true, false>(a, s);
-    return kpad ? launch_fwd_dma_t<D, NW, NBUF, false, true, true>(a, s)
-                : launch_fwd_dma_t<D, NW, NBUF, false, true, false>(a, s);
-  }
-  return causal ? launch_fwd_dma_t<D, NW, NBUF, true, false, false>(a, s)
-                : launch_fwd_dma_t<D, NW, NBUF, false, false, false>(a, s);
-}
-
-template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int ROLE, int MASK = kMaskPlain>
+template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 static hipError_t launch_fwd_stag_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BR = 8 * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_stag_kernel<D, CAUSAL, VARLEN, KPAD, ROLE, MASK>), dim3((unsigned)blocks), dim3(512), 0,
+  hipLaunchKernelGGL((fwd_stag_kernel<D, CAUSAL, VARLEN, KPAD, MASK>), dim3((unsigned)blocks), dim3(512), 0,
                      stream, a, n_qtiles);
   return hipGetLastError();
 }
 
-template <int D, int ROLE>
+template <int D>
 static hipError_t dispatch_fwd_stag(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
   if (varlen) {
-    if (causal) return kpad ? launch_fwd_stag_t<D, true, true, true, ROLE>(a, s)
-                            : launch_fwd_stag_t<D, true, true, false, ROLE>(a, s);
-    return kpad ? launch_fwd_stag_t<D, false, true, true, ROLE>(a, s)
-                : launch_fwd_stag_t<D, false, true, false, ROLE>(a, s);
+    if (causal) return kpad ? launch_fwd_stag_t<D, true, true, true>(a, s)
+                            : launch_fwd_stag_t<D, true, true, false>(a, s);
+    return kpad ? launch_fwd_stag_t<D, false, true, true>(a, s)
+                : launch_fwd_stag_t<D, false, true, false>(a, s);
   }
-  return causal ? launch_fwd_stag_t<D, true, false, false, ROLE>(a, s)
-                : launch_fwd_stag_t<D, false, false, false, ROLE>(a, s);
-}
-
-template <int D, int QB, int NW, int MINB, bool CAUSAL, bool VARLEN, bool KPAD>
-static hipError_t launch_fwd_bf16_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * QB * 32;
-  const int n_qtiles = (a.N + BR - 1) / BR;
-  const int64_t blocks = (int64_t)n_qtiles * a.B * a.H;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, MINB, CAUSAL, VARLEN, KPAD>), dim3((unsigned)blocks),
-                     dim3(NW * 64), 0, stream, a, n_qtiles);
-  return hipGetLastError();
-}
-
-template <int D, int QB, int NW, int MINB>
-static hipError_t dispatch_fwd(const AttnArgs& a, bool causal, bool varlen, bool kpad, hipStream_t s) {
-  if (varlen) {
-    if (causal) return kpad ? launch_fwd_bf16_t<D, QB, NW, MINB, true, true, true>(a, s)
-                            : launch_fwd_bf16_t<D, QB, NW, MINB, true, true, false>(a, s);
-    return kpad ? launch_fwd_bf16_t<D, QB, NW, MINB, false, true, true>(a, s)
-                : launch_fwd_bf16_t<D, QB, NW, MINB, false, true, false>(a, s);
-  }
-  return causal ? launch_fwd_bf16_t<D, QB, NW, MINB, true, false, false>(a, s)
-                : launch_fwd_bf16_t<D, QB, NW, MINB, false, false, false>(a, s);
-}
-
-// Kernel variants.  MIATTN_FWD_TILE=<n> picks one for tuning sweeps:
-//   0 (default) the staggered form, late waves 4-7;
-//   1 the direct-load form (eight waves, three buffers);
-//   2 the staggered form with odd late waves;
-//   3 one 32-row block per wave with register-staged tiles;
-//   4 the four-wave form with 64 rows per wave (fwd_w4.hip);
-//   5 the direct-load form with four waves and two buffers (two
-//     workgroups per CU);
-//   6 the direct-load form with four buffers (loads three tiles ahead);
-//   7 split roles per SIMD (fwd_split.hip, dense layout only).
-static int fwd_tile_choice() {
-  static int choice = [] {
-    const char* e = getenv("MIATTN_FWD_TILE");
-    return e ? atoi(e) : 0;
-  }();
-  return choice;
+  return causal ? launch_fwd_stag_t<D, true, false, false>(a, s)
+                : launch_fwd_stag_t<D, false, false, false>(a, s);
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream) {
   const bool kpad = varlen && a.key_valid != nullptr;
-  const int t = fwd_tile_choice();
-  if (t == 4) return launch_fwd_w4_bf16(a, d, causal, varlen, stream);
-  if (t == 7 && !varlen) return launch_fwd_split_bf16(a, d, causal, stream);
-  if (d == 128) {
-    if (t == 1) return dispatch_fwd_dma<128, 8, 3>(a, causal, varlen, kpad, stream);
-    if (t == 2) return dispatch_fwd_stag<128, 1>(a, causal, varlen, kpad, stream);
-    if (t == 3) return dispatch_fwd<128, 1, 8, 1>(a, causal, varlen, kpad, stream);
-    if (t == 5) return dispatch_fwd_dma<128, 4, 2>(a, causal, varlen, kpad, stream);
-    if (t == 6) return dispatch_fwd_dma<128, 8, 4>(a, causal, varlen, kpad, stream);
-    return dispatch_fwd_stag<128, 0>(a, causal, varlen, kpad, stream);
-  }
-  if (d == 64) {
-    if (t == 1) return dispatch_fwd_dma<64, 8, 3>(a, causal, varlen, kpad, stream);
-    if (t == 2) return dispatch_fwd_stag<64, 1>(a, causal, varlen, kpad, stream);
-    if (t == 3) return dispatch_fwd<64, 1, 8, 1>(a, causal, varlen, kpad, stream);
-    if (t == 5) return dispatch_fwd_dma<64, 4, 2>(a, causal, varlen, kpad, stream);
-    if (t == 6) return dispatch_fwd_dma<64, 8, 4>(a, causal, varlen, kpad, stream);
-    return dispatch_fwd_stag<64, 0>(a, causal, varlen, kpad, stream);
-  }
+  if (d == 128) return dispatch_fwd_stag<128>(a, causal, varlen, kpad, stream);
+  if (d == 64) return dispatch_fwd_stag<64>(a, causal, varlen, kpad, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1091,15 +436,15 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, h
 // block-sparse list (with or without the causal mask): the staggered form.
 hipError_t launch_fwd_masked_bf16(const AttnArgs& a, int d, int mask, bool causal, hipStream_t stream) {
   if (mask == kMaskWindow) {
-    if (d == 128) return launch_fwd_stag_t<128, false, false, false, 0, kMaskWindow>(a, stream);
-    if (d == 64) return launch_fwd_stag_t<64, false, false, false, 0, kMaskWindow>(a, stream);
+    if (d == 128) return launch_fwd_stag_t<128, false, false, false, kMaskWindow>(a, stream);
+    if (d == 64) return launch_fwd_stag_t<64, false, false, false, kMaskWindow>(a, stream);
   } else if (mask == kMaskBlocks) {
     if (d == 128)
-      return causal ? launch_fwd_stag_t<128, true, false, false, 0, kMaskBlocks>(a, stream)
-                    : launch_fwd_stag_t<128, false, false, false, 0, kMaskBlocks>(a, stream);
+      return causal ? launch_fwd_stag_t<128, true, false, false, kMaskBlocks>(a, stream)
+                    : launch_fwd_stag_t<128, false, false, false, kMaskBlocks>(a, stream);
     if (d == 64)
-      return causal ? launch_fwd_stag_t<64, true, false, false, 0, kMaskBlocks>(a, stream)
-                    : launch_fwd_stag_t<64, false, false, false, 0, kMaskBlocks>(a, stream);
+      return causal ? launch_fwd_stag_t<64, true, false, false, kMaskBlocks>(a, stream)
+                    : launch_fwd_stag_t<64, false, false, false, kMaskBlocks>(a, stream);
   }
   return hipErrorInvalidValue;
 }

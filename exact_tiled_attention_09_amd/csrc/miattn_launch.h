@@ -8,8 +8,6 @@ struct DecodeArgs;
 struct Fp8Args;
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
-hipError_t launch_fwd_w4_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
-hipError_t launch_fwd_split_bf16(const AttnArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const AttnArgs& a, int d, bool varlen, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int d, bool causal, bool varlen, hipStream_t stream);
