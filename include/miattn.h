@@ -263,11 +263,14 @@ int attn_quantize_fp8_vt(const void* v, unsigned char* v8t, float* scales, int B
 /* FP8 forward, grouped key/value heads as attn_fwd_gqa: q8, q_scale from
  * attn_quantize_fp8_rows of Q [B,H,N,128]; k8, k_scale of K [B,H_kv,N,128];
  * v8t, v_scale from attn_quantize_fp8_vt of V [B,H_kv,N,128].  o bf16
- * [B,H,N,128], lse fp32 [B,H,N].  The P V product uses P rounded to E4M3
- * (after a power-of-two scaling that keeps every P >= 2^-12 a normal E4M3
- * value), so O differs from exact attention on the dequantized inputs by at
- * most about 2^-4 sum_j P_ij |V_j| per element; LSE is that of the fp32
- * scores.  Fully masked rows and errors as attn_fwd. */
+ * [B,H,N,128], lse fp32 [B,H,N].  The P V product uses P multiplied by 2^6
+ * and rounded to E4M3 (so every P >= 2^-12 is a normal E4M3 value), the 2^6
+ * taken out again with 1/l; so O differs from exact attention on the
+ * dequantized inputs by at most about 2^-4 sum_j P_ij |V_j| per element.
+ * Scores come from FP8 matrix instructions whose accumulation of a score's
+ * 128 products errs by at most 2^-13 of the sum of their magnitudes
+ * (measured through single-key rows, where LSE is the score); LSE is that of
+ * these fp32 scores.  Fully masked rows and errors as attn_fwd. */
 int attn_fwd_fp8(const unsigned char* q8, const float* q_scale, const unsigned char* k8, const float* k_scale,
                  const unsigned char* v8t, const float* v_scale, void* o, float* lse,
                  int B, int H, int H_kv, int N, int d, float scale, int causal, hipStream_t stream);

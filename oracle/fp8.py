@@ -19,10 +19,11 @@ Readings (each listed in the design doc):
     (batch, head).  s and X / s are fp32 divisions (correctly rounded); an
     all-zero block gets s = 1.
   * The reference output is exact attention (this package's definition) on
-    the dequantized tensors s * E4M3value; what the FP8 path adds on top (the
-    rounding of P, scaled by a power of two, to E4M3 for the P V product) is
-    bounded in ``fp8_output_bound``, including P small enough to be an E4M3
-    subnormal after the scaling.
+    the dequantized tensors s * E4M3value.  The pages also round P to FP8 for
+    the P V product but leave open how P is scaled first; what that rounding
+    adds is bounded in ``fp8_output_bound`` for a caller-given power-of-two
+    pre-scale of P (none by default), including P small enough to be an
+    E4M3 subnormal after the scaling.
 """
 from __future__ import annotations
 
@@ -38,7 +39,6 @@ __all__ = [
     "quantize_heads",
     "dequantize_rows",
     "dequantize_heads",
-    "vt_tile_layout",
     "fp8_reference",
     "fp8_output_bound",
 ]
@@ -124,25 +124,6 @@ def dequantize_heads(codes, scales):
     return _VALUES[np.asarray(codes, dtype=np.int64)] * np.asarray(scales, dtype=np.float64)[:, :, None, None]
 
 
-def vt_tile_layout(codes):
-    """V codes [B, H, N, d] -> the transposed tile layout [B, H, ceil(N/64), d, 64]:
-    tile t, feature f, position p holds key 64 t + k(p) with
-    k(p) = 32 (p % 32 // 16) + 8 (p % 16 // 4) + 4 (p // 32) + p % 4;
-    keys past N are 0."""
-    codes = np.asarray(codes, dtype=np.uint8)
-    B, H, N, d = codes.shape
-    nt = -(-N // 64)
-    out = np.zeros((B, H, nt, d, 64), dtype=np.uint8)
-    p = np.arange(64)
-    k_of_p = 32 * ((p % 32) // 16) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
-    for t in range(nt):
-        for pos in range(64):
-            key = 64 * t + int(k_of_p[pos])
-            if key < N:
-                out[:, :, t, :, pos] = codes[:, :, key, :]
-    return out
-
-
 def fp8_reference(q, k, v, scale, causal=False):
     """Quantize bf16-exact inputs as the FP8 path does, then exact attention on
     the dequantized tensors.  q [B, H, N, d], k and v [B, H_kv, N, d].
@@ -157,13 +138,14 @@ def fp8_reference(q, k, v, scale, causal=False):
             "qd": qd, "kd": kd, "vd": vd}
 
 
-def fp8_output_bound(qd, kd, vd, lse, scale, causal=False, p_scale_log2=6):
+def fp8_output_bound(qd, kd, vd, lse, scale, causal=False, p_scale_log2=0):
     """Per-element bound on |O_fp8 - O_ref| from rounding P to E4M3 for the
-    P V product, P being multiplied by 2^p_scale_log2 before rounding.  A P_ij
-    whose scaled value is a normal E4M3 number is off by at most 2^-4 of
-    itself (half an ulp of a 3-bit mantissa); below that (subnormal) it is off
-    by at most half the subnormal step, 2^-10 / 2^p_scale_log2, and never by
-    more than itself.  The error of O_i is at most
+    P V product, P being multiplied by 2^p_scale_log2 before rounding (and
+    divided by it afterwards; p_scale_log2 = 0: no pre-scale).  A P_ij whose
+    scaled value is a normal E4M3 number is off by at most 2^-4 of itself
+    (half an ulp of a 3-bit mantissa); below that (subnormal) it is off by at
+    most half the subnormal step, 2^-10 / 2^p_scale_log2, and never by more
+    than itself.  The error of O_i is at most
     sum_j min(P_ij, max(2^-4 P_ij, 2^-10 / 2^p_scale_log2)) |V_j|.
     Returns (bound, weighted) [B, H, N, d] fp64, weighted = sum_j P_ij |V_j|."""
     B, H, N, d = qd.shape

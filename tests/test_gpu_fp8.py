@@ -3,24 +3,32 @@ attn_quantize_fp8_vt and attn_fwd_fp8.
 
 The quantizers are integer-valued work and must match the oracle bit for bit
 (codes and fp32 scales): ragged N, huge and tiny magnitudes, all-zero blocks.
+attn_quantize_fp8_vt writes its codes in the transposed tile order that
+include/miattn.h declares (tile t, feature f, position p holds key
+64 t + k(p)); the test inverts that declared order on the device's codes and
+compares them with oracle.fp8.quantize_heads, so the oracle knows nothing of
+the kernel's layout.
 
 The forward is checked element by element against exact attention on the
 dequantized inputs (oracle.fp8.fp8_reference, which quantizes the same bf16
 inputs itself), within
     |O - O_ref| <= bound + (2^-8 + delta_i) * weighted + 2^-8 |O_ref|,
-bound the effect of rounding P to E4M3 (oracle.fp8.fp8_output_bound, derived
-and pinned in the oracle's tests: 2^-4 of each P in the normal range, half a
-subnormal step below it) and weighted = sum_j P_ij |V_j|.  The FP8 MFMA accumulates its 64 products with
-a relative error of about 2^-13 of their absolute sum (measured on the
-device); with twice that, a score of row i is off by at most
-delta_i = 2^-12 |scale| max_j sum_f |q_if| |k_jf|, which moves each P_ij by a
-factor e^(+-delta_i) and O_i by at most delta_i * weighted; 2^-8 weighted
-covers the P V accumulation, 2^-8 |O_ref| the bf16 rounding of O.  LSE within
-1e-3 + delta_i (its scores carry the same accumulation error).  At the full-size causal N = 4096 case
-the mean squared error of O against plain bf16 attention on the unquantized
-inputs stays below the 1e-4 the pages quote for FP8 attention at N = 4096
-(short or sharply peaked rows average over few keys, so the figure is only
-checked where the pages give it)."""
+bound the effect of rounding P to E4M3 (oracle.fp8.fp8_output_bound with the
+pre-scale of P by 2^6 that include/miattn.h declares for attn_fwd_fp8;
+derived and pinned in the oracle's tests: 2^-4 of each P in the normal range,
+half a subnormal step below it) and weighted = sum_j P_ij |V_j|.  The scores
+come from FP8 MFMAs, whose accumulation of the 128 products of a score is not
+exact: test_fp8_score_accumulation_error measures it through single-key rows
+(where LSE equals the score) and requires it to stay within 2^-13 of the sum
+of the products' magnitudes.  With twice that, a score of row i is off by at
+most delta_i = 2^-12 |scale| max_j sum_f |q_if| |k_jf|, which moves each P_ij
+by a factor e^(+-delta_i) and O_i by at most delta_i * weighted; 2^-8
+weighted covers the P V accumulation, 2^-8 |O_ref| the bf16 rounding of O.
+LSE within 1e-3 + delta_i (its scores carry the same accumulation error).  At
+the full-size causal N = 4096 case the mean squared error of O against plain
+bf16 attention on the unquantized inputs stays below the 1e-4 the pages quote
+for FP8 attention at N = 4096 (short or sharply peaked rows average over few
+keys, so the figure is only checked where the pages give it)."""
 import math
 import time
 
@@ -80,8 +88,33 @@ def test_quantizers_bit_exact(lib, N, sigma):
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
     np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
     hc, hs = F.quantize_heads(x)
-    np.testing.assert_array_equal(vcodes.cpu().numpy(), F.vt_tile_layout(hc))
+    got, past_end = _untile_vt(vcodes.cpu().numpy(), N)
+    np.testing.assert_array_equal(got, hc)
+    assert np.all(past_end == 0)
     np.testing.assert_array_equal(vscales.cpu().numpy().view(np.uint32), hs.view(np.uint32))
+
+
+# The order attn_quantize_fp8_vt declares in include/miattn.h: position p of a
+# 64-key tile holds key k(p) of the tile.
+_VT_KEY_OF_POS = np.array([32 * ((p % 32) // 16) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
+                           for p in range(64)])
+# attn_fwd_fp8 multiplies P by 2^6 before rounding it to E4M3 (include/miattn.h).
+_P_SCALE_LOG2 = 6
+
+
+def test_declared_vt_order_is_a_permutation():
+    assert sorted(_VT_KEY_OF_POS.tolist()) == list(range(64))
+
+
+def _untile_vt(v8t, N):
+    """[B, H, nt, d, 64] codes in the declared tile order -> [B, H, N, d] codes
+    in key order, plus the codes at positions whose key is past N."""
+    B, H, nt, d, _ = v8t.shape
+    keys = (64 * np.arange(nt)[:, None] + _VT_KEY_OF_POS[None, :]).reshape(-1)   # [nt*64] key of (t, p)
+    flat = np.transpose(v8t, (0, 1, 2, 4, 3)).reshape(B, H, nt * 64, d)        # row (t, p)
+    out = np.zeros((B, H, nt * 64, d), dtype=np.uint8)
+    out[:, :, keys] = flat
+    return out[:, :, :N], out[:, :, N:]
 
 
 def _fwd(lib, q, k, v, scale, causal):
@@ -99,7 +132,8 @@ def _fwd(lib, q, k, v, scale, causal):
 
 def _check(o, lse, q, k, v, scale, causal, mse_bar=None):
     ref = F.fp8_reference(q, k, v, scale, causal)
-    bound, weighted = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], scale, causal)
+    bound, weighted = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], scale, causal,
+                                         p_scale_log2=_P_SCALE_LOG2)
     err = np.abs(o - ref["o"])
     B, H, N, d = q.shape
     G = H // k.shape[1]
@@ -124,6 +158,39 @@ def _check(o, lse, q, k, v, scale, causal, mse_bar=None):
     _say(f"  MSE vs bf16 attention {mse:.2e}")
     if mse_bar is not None:
         assert mse <= mse_bar
+
+
+def test_fp8_score_accumulation_error(lib):
+    """A row that sees a single key has LSE equal to its score, so single-key
+    problems (N = 1) expose the FP8 MFMA's accumulation of the 128 products of
+    a score.  Inputs are 2^-3 times E4M3 values with a 56 = 448 / 8 entry in
+    each row, so quantization is lossless (scale exactly 1/8) and the exact
+    score is the fp64 dot product of the bf16 inputs.  Signs are random, so
+    the products cancel.  Bar: |LSE - score| <= 2^-13 |scale| sum_f |q_f k_f|
+    plus four fp32 roundings of the score."""
+    vals = F.e4m3_values()
+    fin = np.array([c for c in range(1, 0x7F) if vals[c] <= 240])
+    rng = np.random.default_rng(11)
+    B, H, d = 64, 16, 128
+
+    def draw():
+        x = vals[rng.choice(fin, size=(B, H, 1, d))] * np.where(rng.random((B, H, 1, d)) < 0.5, -1.0, 1.0) / 8
+        x[..., 0] = 56.0 * np.where(rng.random((B, H, 1)) < 0.5, -1.0, 1.0)
+        return x.astype(np.float32)
+
+    q, k, v = draw(), draw(), draw()
+    rq, sq = F.quantize_rows(q)
+    assert np.all(sq == np.float32(0.125)) and np.array_equal(F.dequantize_rows(rq, sq), q.astype(np.float64))
+    worst = 0.0
+    for scale in (1 / math.sqrt(128), 0.5, -0.3):
+        _, lse = _fwd(lib, q, k, v, scale, False)
+        score = scale * np.sum(q.astype(np.float64) * k, axis=3)[..., 0]
+        mag = abs(scale) * np.sum(np.abs(q.astype(np.float64) * k), axis=3)[..., 0]
+        err = np.abs(lse[..., 0] - score)
+        allowed = 2.0 ** -13 * mag + 4 * 2.0 ** -24 * np.abs(score)
+        worst = max(worst, float(np.max((err - 4 * 2.0 ** -24 * np.abs(score)) / mag)))
+        assert np.all(err <= allowed), f"scale {scale}: accumulation error above 2^-13 of sum |q k|"
+    _say(f"  FP8 score accumulation: worst |error| / sum |q k| = {worst:.3e} = 2^{math.log2(max(worst, 1e-30)):.2f}")
 
 
 @pytest.mark.parametrize("causal", [False, True])

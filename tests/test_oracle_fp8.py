@@ -7,10 +7,9 @@
 * Per-block quantization: each block's largest magnitude lands on +-448,
   power-of-two scaling of the input changes only the scale, the relative
   error of every normal code is at most 2^-4, all-zero blocks.
-* The transposed V tile layout against the accumulator's key order written
-  out independently.
 * The FP8 reference equals exact attention when quantization is lossless,
-  and the error bound covers an explicit simulation of rounding P to E4M3."""
+  and the error bound covers an explicit simulation of rounding P to E4M3,
+  with and without a power-of-two pre-scale of P."""
 import os
 import types
 
@@ -96,27 +95,6 @@ def test_block_quantization_properties():
     assert sv.shape == (2, 3) and np.all(sv == np.max(np.abs(x), axis=(2, 3)) / np.float32(448))
 
 
-def test_vt_tile_layout_is_the_accumulator_key_order():
-    """Position p = 32 hi + 16 kb + r of a tile holds the key that lane half
-    hi finds in accumulator register r of key block kb: 32 kb + 8 (r // 4) +
-    4 hi + r % 4."""
-    rng = np.random.default_rng(2)
-    codes = rng.integers(0, 0x7E, size=(1, 2, 150, 8), dtype=np.uint8)
-    out = F.vt_tile_layout(codes)
-    assert out.shape == (1, 2, 3, 8, 64)
-    seen = set()
-    for hi in range(2):
-        for kb in range(2):
-            for r in range(16):
-                pos = 32 * hi + 16 * kb + r
-                key = 32 * kb + 8 * (r // 4) + 4 * hi + r % 4
-                seen.add(key)
-                for t in range(3):
-                    want = codes[:, :, 64 * t + key, :] if 64 * t + key < 150 else 0
-                    np.testing.assert_array_equal(out[:, :, t, :, pos], want)
-    assert seen == set(range(64))
-
-
 def test_lossless_quantization_gives_exact_attention():
     """Inputs whose blocks are 2^-3 times E4M3 values with a +-448 entry in
     every block quantize exactly, so the reference is plain attention."""
@@ -133,27 +111,43 @@ def test_lossless_quantization_gives_exact_attention():
     np.testing.assert_allclose(ref["lse"], lse, rtol=0, atol=1e-12)
 
 
-def test_bound_covers_rounding_p_to_e4m3():
-    """Rounding P (times a power of two) to E4M3 before P V moves O by no more
-    than fp8_output_bound."""
-    rng = np.random.default_rng(4)
-    q, k, v = (rng.standard_normal((1, 2, 96, 16)).astype(np.float32) for _ in range(3))
-    for sig, sc in ((1.0, 0.25), (3.0, 0.9)):   # the second has many P below 2^-12 (subnormal after x 2^6)
+@pytest.mark.parametrize("p_log2", [0, 6])
+def test_bound_covers_rounding_p_to_e4m3(p_log2):
+    """Rounding P (times 2^p_log2) to E4M3 before P V moves O by no more than
+    fp8_output_bound with the same pre-scale; the second case of each pre-scale
+    has many P in the E4M3 subnormal range after the scaling."""
+    rng = np.random.default_rng(4 + p_log2)
+    for sig, sc in ((1.0, 0.25), (3.0, 0.9)):
         q, k, v = (rng.standard_normal((1, 2, 96, 16)).astype(np.float32) * sig for _ in range(3))
         ref = F.fp8_reference(q, k, v, sc, causal=True)
-        bound, weighted = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], sc, causal=True)
-        assert np.all(bound <= 2.0 ** -4 * weighted + 1e-300 + 2.0 ** -16 * np.abs(ref["vd"]).sum(axis=2)[:, :, None])
+        bound, weighted = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], sc, causal=True,
+                                             p_scale_log2=p_log2)
+        floor_ = 2.0 ** -10 / 2.0 ** p_log2 * np.abs(ref["vd"]).sum(axis=2)[:, :, None]
+        assert np.all(bound <= 2.0 ** -4 * weighted + floor_ + 1e-300)
         tight = 0.0
+        pre = 2.0 ** p_log2
         for h in range(2):
             s = sc * ref["qd"][0, h] @ ref["kd"][0, h].T
             s = np.where(np.tril(np.ones((96, 96), bool)), s, -np.inf)
             p = np.exp(s - ref["lse"][0, h][:, None])
-            pq = V[F.e4m3_encode((p * 64).astype(np.float32))] / 64
+            pq = V[F.e4m3_encode((p * pre).astype(np.float32))] / pre
             o_sim = pq @ ref["vd"][0, h]
             err = np.abs(o_sim - ref["o"][0, h])
             assert np.all(err <= bound[0, h] * (1 + 1e-9) + 1e-15)
             tight = max(tight, float(np.max(err / np.maximum(bound[0, h], 1e-300))))
         assert tight > 0.2   # the bound is not vacuous
+
+
+def test_bound_without_prescale_is_wider_below_the_normal_range():
+    """Without a pre-scale every P below 2^-6 is an E4M3 subnormal, so the
+    bound's floor is 2^-10 per unit |V| against 2^-16 with a 2^6 pre-scale."""
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((1, 1, 64, 16)).astype(np.float32) for _ in range(3))
+    ref = F.fp8_reference(q, k, v, 0.25, causal=False)
+    b0, w = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], 0.25)
+    b6, _ = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], 0.25, p_scale_log2=6)
+    assert np.all(b6 <= b0 + 1e-300) and np.any(b6 < b0)
+    assert np.all(b6 >= 0) and np.all(b0 <= 2.0 ** -4 * w + 2.0 ** -10 * np.abs(ref["vd"]).sum(axis=2)[:, :, None])
 
 
 def _mutant(old, new):
