@@ -13,6 +13,8 @@ script.  Functions carry the C names and take device tensors:
     attn_quantize_fp8_rows, attn_quantize_fp8_vt, attn_fwd_fp8,
     attn_fwd_f32, attn_bwd_f32, attn_bwd_f32_workspace_bytes,
     attn_fwd_varlen, attn_bwd_varlen, attn_bwd_varlen_workspace_bytes
+
+plus check_cu_seqlens (host-side validation of packed offsets).
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
@@ -42,6 +44,7 @@ from ._lib import (  # noqa: F401
     attn_fwd_varlen,
     attn_quantize_fp8_rows,
     attn_quantize_fp8_vt,
+    check_cu_seqlens,
     load,
     miattn_status_string,
     miattn_version,

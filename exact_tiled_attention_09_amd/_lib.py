@@ -387,10 +387,37 @@ def _varlen_specs(fn, T, H, d, cu_seqlens, key_valid, **tensors):
     _expect(fn, *specs)
 
 
+def check_cu_seqlens(cu_seqlens_host, total_tokens: int, max_seqlen: int, fn: str = "cu_seqlens") -> None:
+    """Validate a host copy of the cumulative offsets before a packed call.
+
+    The library reads cu_seqlens from device memory and cannot check it
+    without a device-to-host copy; a caller that holds the offsets on the host
+    passes them here (or as `cu_seqlens_host=` to the packed wrappers): they
+    must start at 0, never decrease, end at total_tokens, and no sequence may
+    be longer than max_seqlen."""
+    cu = [int(x) for x in (cu_seqlens_host.tolist() if hasattr(cu_seqlens_host, "tolist") else cu_seqlens_host)]
+    if len(cu) < 2:
+        raise ValueError(f"{fn}: cu_seqlens needs at least two entries")
+    if cu[0] != 0:
+        raise ValueError(f"{fn}: cu_seqlens[0] is {cu[0]}, expected 0")
+    if cu[-1] != total_tokens:
+        raise ValueError(f"{fn}: cu_seqlens[-1] is {cu[-1]}, expected total_tokens = {total_tokens}")
+    for i in range(len(cu) - 1):
+        step = cu[i + 1] - cu[i]
+        if step < 0:
+            raise ValueError(f"{fn}: cu_seqlens decreases at entry {i + 1}")
+        if step > max_seqlen:
+            raise ValueError(f"{fn}: sequence {i} has {step} tokens, more than max_seqlen = {max_seqlen}")
+
+
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool,
-                    key_valid=None, stream=None):
+                    key_valid=None, stream=None, cu_seqlens_host=None):
     T, H, d = _varlen_dims(q)
     _varlen_specs("attn_fwd_varlen", T, H, d, cu_seqlens, key_valid, q=q, k=k, v=v, o=o, lse=lse)
+    if cu_seqlens_host is not None:
+        if len(cu_seqlens_host) != int(cu_seqlens.numel()):
+            raise ValueError("attn_fwd_varlen: cu_seqlens_host and cu_seqlens differ in length")
+        check_cu_seqlens(cu_seqlens_host, T, int(max_seqlen), "attn_fwd_varlen")
     nseq = int(cu_seqlens.numel()) - 1
     _check("attn_fwd_varlen", load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                                      _ptr(cu_seqlens), nseq, int(max_seqlen), T, H, d,
@@ -403,10 +430,14 @@ def attn_bwd_varlen_workspace_bytes(total_tokens: int, H: int, d: int) -> int:
 
 
 def attn_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens, max_seqlen: int, scale: float, causal: bool,
-                    workspace, key_valid=None, stream=None):
+                    workspace, key_valid=None, stream=None, cu_seqlens_host=None):
     T, H, d = _varlen_dims(q)
     _varlen_specs("attn_bwd_varlen", T, H, d, cu_seqlens, key_valid, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq,
                   dk=dk, dv=dv)
+    if cu_seqlens_host is not None:
+        if len(cu_seqlens_host) != int(cu_seqlens.numel()):
+            raise ValueError("attn_bwd_varlen: cu_seqlens_host and cu_seqlens differ in length")
+        check_cu_seqlens(cu_seqlens_host, T, int(max_seqlen), "attn_bwd_varlen")
     nseq = int(cu_seqlens.numel()) - 1
     _check("attn_bwd_varlen", load().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq,

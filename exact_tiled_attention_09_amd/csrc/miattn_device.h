@@ -165,15 +165,18 @@ __device__ __forceinline__ SeqView seq_view(const AttnArgs& a, int b, int h, int
   SeqView s;
   const int hk = h / (a.H / a.Hkv);
   if constexpr (VARLEN) {
-    const int t0 = a.cu_seqlens[b];
-    const int t1 = a.cu_seqlens[b + 1];
+    // Offsets are clamped into [0, total_tokens] and the length to [0, N]
+    // (the longest sequence), so malformed offsets cannot address memory
+    // outside the packed tensors: rows past the clamp are simply not written.
+    const int t0 = min(max(a.cu_seqlens[b], 0), a.total_tokens);
+    const int t1 = min(max(a.cu_seqlens[b + 1], t0), a.total_tokens);
     s.base = ((int64_t)t0 * a.H + h) * D;
     s.tok_stride = (int64_t)a.H * D;
     s.kv_base = ((int64_t)t0 * a.Hkv + hk) * D;
     s.kv_stride = (int64_t)a.Hkv * D;
     s.row_base = (int64_t)h * a.total_tokens + t0;
     s.tok0 = t0;
-    s.len = t1 - t0;
+    s.len = min(t1 - t0, a.N);
   } else {
     s.base = ((int64_t)b * a.H + h) * (int64_t)a.N * D;
     s.tok_stride = D;

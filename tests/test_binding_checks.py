@@ -2,6 +2,7 @@
 problem, before anything reaches the library (the C ABI sees raw pointers,
 so such a tensor would make a kernel read or write past its buffer).  Host
 logic only: CPU tensors, no library call."""
+import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -78,3 +79,16 @@ def test_decode_fp8_and_packed_shapes():
         M.attn_fwd_varlen(pq, pq, pq, pq, plse, cu, 60, 0.125, True, key_valid=torch.ones(99, dtype=torch.uint8))
     with pytest.raises(ValueError, match="cu_seqlens is torch.int64"):
         M.attn_fwd_varlen(pq, pq, pq, pq, plse, cu.long(), 60, 0.125, True)
+
+
+def test_host_cu_seqlens_check():
+    """check_cu_seqlens refuses offsets the kernels would misread: not
+    starting at 0, decreasing, not ending at total_tokens, a sequence longer
+    than max_seqlen."""
+    from exact_tiled_attention_09_amd import check_cu_seqlens
+    check_cu_seqlens([0, 5, 5, 12], 12, 7)
+    check_cu_seqlens(np.array([0, 64], np.int32), 64, 64)
+    for cu, T, m in (([1, 5, 12], 12, 7), ([0, 6, 5, 12], 12, 7), ([0, 5, 11], 12, 7), ([0, 5, 13], 13, 7),
+                     ([0], 0, 1)):
+        with pytest.raises(ValueError):
+            check_cu_seqlens(cu, T, m)
