@@ -108,7 +108,9 @@ __global__ void __launch_bounds__(64, 1) fwd_f32_kernel(AttnArgs a, int n_qtiles
 
   const float lt = wave_sum_halves(l);
   if (qi < sv.len) {
-    const bool dead = (m == kNegInf) || !(lt > 0.f);
+    // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
+    // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
+    const bool dead = (m == kNegInf) && !(lt != lt);
     const float inv = dead ? 0.f : 1.f / lt;
     float* __restrict__ op = (float*)a.o + sv.base + (int64_t)qi * D;
 #pragma unroll

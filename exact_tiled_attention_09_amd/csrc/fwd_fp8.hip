@@ -402,7 +402,9 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   const float lt = wave_sum_halves(l);
   const int qi = q_wave0 + l32;
   if (qi < len) {
-    const bool dead = (m == kNegInf) || !(lt > 0.f);
+    // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
+    // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
+    const bool dead = (m == kNegInf) && !(lt != lt);
     const float inv = dead ? 0.f : a.v_scale[bhk] / lt;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
