@@ -81,3 +81,45 @@ def check_f32(gpu, ref, what, tol=F32_MAX_ABS):
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
     assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.0e}"
     return err
+
+
+def tile_rel_fro_max(gpu, ref, tile=64) -> float:
+    """Largest relative Frobenius error over consecutive blocks of `tile` rows
+    (a diagnostic beside the whole-head bar: one bad 32-row block can hide in
+    a head-wide norm)."""
+    a = np.asarray(gpu, np.float64)
+    b = np.asarray(ref, np.float64)
+    worst = 0.0
+    for r0 in range(0, a.shape[0], tile):
+        den = float(np.linalg.norm(b[r0:r0 + tile]))
+        if den > 0.0:
+            worst = max(worst, float(np.linalg.norm(a[r0:r0 + tile] - b[r0:r0 + tile])) / den)
+    return worst
+
+
+def host_workers() -> int:
+    """Worker threads for oracle work on the host: the cores this process may
+    use, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def map_heads(fn, jobs):
+    """Run fn(job) for every job on a thread pool, one BLAS thread per worker
+    (numpy's large array operations release the GIL, so the heads run in
+    parallel).  Returns the results in job order; the first failure raises."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(host_workers()) as ex:
+            return list(ex.map(fn, jobs))
+
+
+def sample_positions(n: int, count: int, rng) -> np.ndarray:
+    """`count` distinct positions of [0, n) including the first two and the
+    last two, the rest drawn by rng; sorted."""
+    fixed = sorted({0, 1, n - 2, n - 1} & set(range(n)))
+    rest = np.setdiff1d(np.arange(n), fixed)
+    extra = rng.choice(rest, size=min(len(rest), max(0, count - len(fixed))), replace=False)
+    return np.sort(np.concatenate([np.asarray(fixed, np.int64), extra.astype(np.int64)]))

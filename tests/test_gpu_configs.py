@@ -1,12 +1,19 @@
 """GPU parity at the five workload configurations, at full size, through the
 same entry points and launch configuration the benchmark times.
 
-The fp64 oracle checks whole heads element by element on a sample of heads
-(and sampled rows / key columns where a whole head is too large for the CPU
-within the test's time); properties that hold at any size are checked on
-every head: finite outputs, the -inf pattern of LSE, and for causal problems
-the first row of every head (it sees one key: O_0 = V_0 exactly, LSE_0 =
-scale * q_0 . k_0)."""
+Every head of every configuration is compared with the fp64 oracle:
+  * whole heads element by element for a few heads per configuration (with
+    the largest relative Frobenius error over 64-row tiles printed beside the
+    head-wide bar);
+  * every other head through oracle.attention.head_backward_sampled: O and
+    LSE of every row of the head, dQ at 32 query rows and dK, dV at 32 key
+    columns (always including the first two and last two of the head);
+    packed sequences: 8 rows and 8 key columns of every sequence of every
+    head.
+Properties that hold at any size are checked too: finite outputs, the -inf
+pattern of LSE, and for causal problems the first row of every head (it sees
+one key: O_0 = V_0 exactly, LSE_0 = scale * q_0 . k_0).  The oracle work runs
+on a thread pool over the host's cores."""
 import math
 import time
 
@@ -15,7 +22,8 @@ import pytest
 
 from attn_inputs import dense_inputs, left_padding_key_mask, varlen_inputs
 from oracle import attention as A
-from parity_utils import (BF16_O_MAX_ABS, LSE_MAX_ABS, check_bf16, check_f32, check_lse, to_dev, to_np)
+from parity_utils import (BF16_O_MAX_ABS, LSE_MAX_ABS, check_bf16, check_f32, check_lse, map_heads,
+                          sample_positions, tile_rel_fro_max, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,8 +89,48 @@ def _check_heads(out, inp, scale, causal, heads, bwd):
         check_lse(to_np(out["lse"][b, h]), lse)
         if bwd:
             for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
-                fro, mab = check_bf16(to_np(out[name][b, h]), ref, f"{name}[{b},{h}]")
-                _say(f"  {name}: rel-fro {fro:.2e} max-abs {mab:.2e}")
+                g = to_np(out[name][b, h])
+                fro, mab = check_bf16(g, ref, f"{name}[{b},{h}]")
+                _say(f"  {name}: rel-fro {fro:.2e} max-abs {mab:.2e} worst 64-row tile {tile_rel_fro_max(g, ref):.2e}")
+
+
+def _host_outputs(out):
+    """Device outputs -> float32 numpy (bf16 values are exact in float32)."""
+    return {n: t.detach().float().cpu().numpy() for n, t in out.items()}
+
+
+def _sampled_dense_head(job):
+    """One head against head_backward_sampled: O and LSE of every row, dQ at
+    the sampled rows, dK and dV at the sampled key columns."""
+    label, q, k, v, do, scale, causal, rows, cols, g = job
+    dq, dk, dv, o, lse, _ = A.head_backward_sampled(q, k, v, do, scale, causal, None, rows, cols)
+    fo, _ = check_bf16(g["o"], o, f"O{label}", max_abs_tol=BF16_O_MAX_ABS)
+    check_lse(g["lse"], lse, what=f"LSE{label}")
+    res = {"o": fo, "o_tile": tile_rel_fro_max(g["o"], o)}
+    if dq is not None and "dq" in g:
+        res["dq"] = check_bf16(g["dq"], dq, f"dq{label} rows")[0]
+        res["dk"] = check_bf16(g["dk"], dk, f"dk{label} cols")[0]
+        res["dv"] = check_bf16(g["dv"], dv, f"dv{label} cols")[0]
+    return res
+
+
+def _every_head(inp, outh, scale, causal, heads, bwd, seed):
+    """Sampled oracle check of the given (b, h) heads, in parallel."""
+    jobs = []
+    N = inp["q"].shape[2]
+    for (b, h) in heads:
+        rng = np.random.default_rng(seed * 100003 + b * 1009 + h)
+        rows = sample_positions(N, 32, rng)
+        cols = sample_positions(N, 32, rng)
+        g = {"o": outh["o"][b, h], "lse": outh["lse"][b, h]}
+        if bwd:
+            g.update(dq=outh["dq"][b, h][rows], dk=outh["dk"][b, h][cols], dv=outh["dv"][b, h][cols])
+        jobs.append((f"[{b},{h}]", inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
+                     inp["do"][b, h] if bwd else inp["q"][b, h], scale, causal,
+                     rows if bwd else [], cols if bwd else [], g))
+    res = map_heads(_sampled_dense_head, jobs)
+    worst = {key: max(r[key] for r in res) for key in res[0]}
+    _say(f"  {len(heads)} heads sampled; worst rel-fro " + ", ".join(f"{k_} {v_:.2e}" for k_, v_ in worst.items()))
 
 
 def test_config2_fwd_noncausal_d64(lib):
@@ -92,16 +140,33 @@ def test_config2_fwd_noncausal_d64(lib):
     out = _dense_run(lib, inp, 1 / 8, False, bwd=False)
     _all_heads_properties(out, inp, 1 / 8, False)
     _check_heads(out, inp, 1 / 8, False, [(0, 0), (3, 9), (7, 15)], bwd=False)
+    _every_head(inp, _host_outputs(out), 1 / 8, False, [(b, h) for b in range(8) for h in range(16)], False, 2)
 
 
-def test_config3_fwd_bwd_causal_d128(lib):
-    """B=4, H=32, N=4096, d=128, bf16 causal forward and backward, seed 0."""
+@pytest.fixture(scope="module")
+def config3(lib):
+    """B=4, H=32, N=4096, d=128, bf16 causal forward and backward, seed 0:
+    inputs and the GPU's outputs on the host."""
     _say("config 3: generate")
     inp = dense_inputs(4, 32, 4096, 128, "bf16", seed=0)
     scale = 1 / math.sqrt(128)
     out = _dense_run(lib, inp, scale, True, bwd=True)
     _all_heads_properties(out, inp, scale, True)
+    return inp, out, _host_outputs(out), scale
+
+
+def test_config3_fwd_bwd_causal_d128(config3):
+    """Three whole heads element by element."""
+    inp, out, _, scale = config3
     _check_heads(out, inp, scale, True, [(0, 0), (2, 17), (3, 31)], bwd=True)
+
+
+@pytest.mark.parametrize("batch", [0, 1, 2, 3])
+def test_config3_every_head_sampled(config3, batch):
+    """All 32 heads of one batch entry against the sampled oracle."""
+    inp, _, outh, scale = config3
+    _say(f"config 3: batch {batch}, every head sampled")
+    _every_head(inp, outh, scale, True, [(batch, h) for h in range(32)], True, 3)
 
 
 def test_short_sequences_noncausal_d64(lib):
@@ -113,6 +178,7 @@ def test_short_sequences_noncausal_d64(lib):
     out = _dense_run(lib, inp, 1 / 8, False, bwd=True)
     _all_heads_properties(out, inp, 1 / 8, False)
     _check_heads(out, inp, 1 / 8, False, [(0, 0), (31, 7), (63, 15)], bwd=True)
+    _every_head(inp, _host_outputs(out), 1 / 8, False, [(b, h) for b in range(64) for h in range(16)], True, 6)
 
 
 def test_d_prepass_benchmark_shape(lib):
@@ -147,30 +213,34 @@ def test_d_prepass_benchmark_shape(lib):
     assert torch.equal(ws[: B * H * N * 4].view(torch.float32).view(B, H, N), d_gpu)
 
 
-def test_config4_long_sequence_sharp_scores(lib):
+@pytest.fixture(scope="module")
+def config4(lib):
     """B=1, H=16, N=16384, d=128, causal, Q and K ~ N(0, 1.5^2): the running
-    max moves often.  Head 0 is checked whole; head 15 at sampled query rows
-    and key columns."""
+    max moves often."""
     _say("config 4: generate")
     inp = dense_inputs(1, 16, 16384, 128, "bf16", seed=0, sigma_qk=1.5)
     scale = 1 / math.sqrt(128)
     out = _dense_run(lib, inp, scale, True, bwd=True)
     _all_heads_properties(out, inp, scale, True)
+    return inp, out, _host_outputs(out), scale
+
+
+def test_config4_long_sequence_sharp_scores(config4):
+    """Head 0 whole, element by element."""
+    inp, out, _, scale = config4
     _check_heads(out, inp, scale, True, [(0, 0)], bwd=True)
-    rng = np.random.default_rng(1)
-    rows = np.sort(np.concatenate([[0, 1, 16383], rng.choice(16384, 61, replace=False)]))
-    cols = np.sort(np.concatenate([[0, 1, 16383], rng.choice(16384, 61, replace=False)]))
-    _say("oracle sampled head 15")
-    dq, dk, dv, o, lse, _ = A.head_backward_sampled(inp["q"][0, 15], inp["k"][0, 15], inp["v"][0, 15],
-                                                    inp["do"][0, 15], scale, True, None, rows, cols)
-    check_bf16(to_np(out["o"][0, 15]), o, "O[0,15]", max_abs_tol=BF16_O_MAX_ABS)
-    check_lse(to_np(out["lse"][0, 15]), lse)
-    check_bf16(to_np(out["dq"][0, 15])[rows], dq, "dq[0,15] rows")
-    check_bf16(to_np(out["dk"][0, 15])[cols], dk, "dk[0,15] cols")
-    check_bf16(to_np(out["dv"][0, 15])[cols], dv, "dv[0,15] cols")
 
 
-def test_config5_varlen_keypad_causal(lib):
+@pytest.mark.parametrize("part", [0, 1, 2, 3])
+def test_config4_every_head_sampled(config4, part):
+    """Heads 4 part .. 4 part + 3 against the sampled oracle."""
+    inp, _, outh, scale = config4
+    _say(f"config 4: heads {4 * part}..{4 * part + 3} sampled")
+    _every_head(inp, outh, scale, True, [(0, h) for h in range(4 * part, 4 * part + 4)], True, 4)
+
+
+@pytest.fixture(scope="module")
+def config5(lib):
     """16 packed sequences with lengths uniform in [64, 8192], H=32, d=128,
     causal, with left key padding that fully masks ~1% of query rows."""
     import torch
@@ -185,13 +255,23 @@ def test_config5_varlen_keypad_causal(lib):
     kv_d = torch.from_numpy(kv).cuda()
     o = torch.empty_like(q)
     lse = torch.empty((32, T), dtype=torch.float32, device="cuda")
-    lib.attn_fwd_varlen(q, k, v, o, lse, cu_d, inp["max_seqlen"], scale, True, kv_d)
+    lib.attn_fwd_varlen(q, k, v, o, lse, cu_d, inp["max_seqlen"], scale, True, kv_d, cu_seqlens_host=cu)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(lib.attn_bwd_varlen_workspace_bytes(T, 32, 128), dtype=torch.uint8, device="cuda")
-    lib.attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_d, inp["max_seqlen"], scale, True, ws, kv_d)
+    lib.attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_d, inp["max_seqlen"], scale, True, ws, kv_d,
+                        cu_seqlens_host=cu)
     torch.cuda.synchronize()
-    out = {n: to_np(t) for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
-    # every head: the fully masked rows are exactly the left-padded positions
+    out = {n: t.float().cpu().numpy() for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+    return inp, kv, out, scale
+
+
+def test_config5_varlen_keypad_causal(config5):
+    """Every head: the fully masked rows are exactly the left-padded
+    positions, with O = 0 and zero gradients; head 5 over every sequence and
+    head 30 over the two shortest, whole."""
+    inp, kv, out, scale = config5
+    cu = inp["cu_seqlens"]
+    T = int(cu[-1])
     dead_expected = np.zeros(T, bool)
     for s in range(16):
         dead_expected[cu[s]:cu[s + 1]] = np.cumsum(kv[cu[s]:cu[s + 1]]) == 0
@@ -203,7 +283,6 @@ def test_config5_varlen_keypad_causal(lib):
     assert np.all(out["dk"][kv == 0] == 0) and np.all(out["dv"][kv == 0] == 0)
     for name in ("o", "dq", "dk", "dv"):
         assert np.all(np.isfinite(out[name])), name
-    # head 5: every sequence, whole; head 30: the two shortest sequences, whole
     lengths = np.diff(cu)
     for h, seqs in ((5, list(range(16))), (30, list(np.argsort(lengths)[:2]))):
         _say(f"oracle head {h} over {len(seqs)} sequences")
@@ -214,8 +293,49 @@ def test_config5_varlen_keypad_causal(lib):
         check_bf16(out["o"][sel, h], ref["o"][sel, h], f"O[:, {h}]", max_abs_tol=BF16_O_MAX_ABS)
         check_lse(out["lse"][h, sel], ref["lse"][h, sel])
         for name in ("dq", "dk", "dv"):
-            fro, mab = check_bf16(out[name][sel, h], ref[name][sel, h], f"{name}[:, {h}]")
-            _say(f"  {name}: rel-fro {fro:.2e} max-abs {mab:.2e}")
+            g = out[name][sel, h]
+            fro, mab = check_bf16(g, ref[name][sel, h], f"{name}[:, {h}]")
+            _say(f"  {name}: rel-fro {fro:.2e} max-abs {mab:.2e} worst 64-row tile "
+                 f"{tile_rel_fro_max(g, ref[name][sel, h]):.2e}")
+
+
+def _sampled_packed_head(job):
+    """One head of the packed problem: every sequence through
+    head_backward_sampled (O and LSE of every row, dQ at 8 rows and dK, dV at
+    8 key columns per sequence); the bar applies over the head's samples."""
+    h, inp, kv, out, scale = job
+    cu = inp["cu_seqlens"]
+    rng = np.random.default_rng(5000 + h)
+    acc = {n: ([], []) for n in ("o", "dq", "dk", "dv")}
+    for s in range(len(cu) - 1):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        L = t1 - t0
+        rows = sample_positions(L, 8, rng)
+        cols = sample_positions(L, 8, rng)
+        sl = slice(t0, t1)
+        dq, dk, dv, o, lse, _ = A.head_backward_sampled(inp["q"][sl, h], inp["k"][sl, h], inp["v"][sl, h],
+                                                        inp["do"][sl, h], scale, True, kv[sl], rows, cols)
+        check_lse(out["lse"][h, sl], lse, what=f"LSE[seq {s}, head {h}]")
+        for name, got, ref in (("o", out["o"][sl, h], o), ("dq", out["dq"][sl, h][rows], dq),
+                               ("dk", out["dk"][sl, h][cols], dk), ("dv", out["dv"][sl, h][cols], dv)):
+            acc[name][0].append(got)
+            acc[name][1].append(ref)
+    res = {}
+    for name, (gs, rs) in acc.items():
+        g, r = np.concatenate(gs), np.concatenate(rs)
+        res[name] = check_bf16(g, r, f"{name}[head {h}] samples",
+                               max_abs_tol=BF16_O_MAX_ABS if name == "o" else None)[0]
+    return res
+
+
+@pytest.mark.parametrize("part", [0, 1, 2, 3])
+def test_config5_every_head_sampled(config5, part):
+    """Heads 8 part .. 8 part + 7, every sequence, against the sampled oracle."""
+    inp, kv, out, scale = config5
+    _say(f"config 5: heads {8 * part}..{8 * part + 7} sampled")
+    res = map_heads(_sampled_packed_head, [(h, inp, kv, out, scale) for h in range(8 * part, 8 * part + 8)])
+    worst = {key: max(r[key] for r in res) for key in res[0]}
+    _say("  worst rel-fro " + ", ".join(f"{k_} {v_:.2e}" for k_, v_ in worst.items()))
 
 
 def test_config1_fwd_bwd_f32(lib):
