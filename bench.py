@@ -25,7 +25,11 @@ intensity against the machine balance (2516.6 TFLOP/s / 8 TB/s): below it the
 kernel is HBM-bound and reported in GB/s.
 
 Other workloads: the D pre-pass alone (attn_bwd_preprocess, HBM-bound),
-decoding against a KV cache (HBM-bound) and the FP8 forward.
+decoding against a KV cache (HBM-bound), the FP8 forward, packed
+variable-length sequences with key padding, and the small fp32 problem.
+
+The CPU baseline runs the fp64 oracle on the host with its BLAS threads
+pinned to the cores of this process's affinity set (the count reported).
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -74,6 +78,16 @@ PEAK_FP8_TFLOPS = 5033.2    # 2 x the bf16 dense peak
 PREP_WORKLOADS = {
     "prep_b4_h32_n4096_d128": dict(B=4, H=32, N=4096, d=128),
 }
+# packed variable-length sequences: 16 sequences, lengths uniform in [64, 8192] (seed 0), H32 d128, causal,
+# left key padding of max(1, round(0.01 L)) tokens per sequence (fully masks ~1% of the query rows)
+VARLEN_WORKLOADS = {
+    "varlen_causal_keypad_h32_d128": dict(nseq=16, len_lo=64, len_hi=8192, H=32, d=128, causal=True, pad=0.01),
+}
+# the fp32 problem: B1 H1 N128 d64, non-causal, scale 1/8 (latency-bound: one workgroup per 32 query rows)
+F32_WORKLOADS = {
+    "f32_b1_h1_n128_d64": dict(B=1, H=1, N=128, d=64, causal=False),
+}
+PEAK_FP32_MFMA_TFLOPS = 157.3
 # decoding: one new token per sequence against a 32768-token KV cache
 DECODE_WORKLOADS = {
     "decode_b8_h32_hkv8_n32768_d128": dict(B=8, H=32, Hkv=8, N=32768, d=128),
@@ -233,26 +247,47 @@ class no_gc:
         return False
 
 
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity set)."""
+    return len(os.sched_getaffinity(0))
+
+
+class pinned_blas:
+    """Runs the oracle with its BLAS threads pinned to the host cores this
+    process may use, so that the core count the baseline reports is the one it
+    ran on."""
+
+    def __enter__(self):
+        from threadpoolctl import threadpool_limits
+        self.cores = host_cores()
+        self.ctl = threadpool_limits(limits=self.cores, user_api="blas")
+        return self
+
+    def __exit__(self, *exc):
+        self.ctl.restore_original_limits()
+        return False
+
+
 def cpu_baseline(inp, cfg, scale, budget_s=10.0):
     """The fp64 oracle, forward + backward, on whole (b, h) heads of the same
     inputs, head after head until about ``budget_s`` seconds of host time
     have been spent (at least one head, at most all of them); the rate is
     scaled to the whole batch.  A reported baseline, not a target."""
-    from threadpoolctl import threadpool_info
     from oracle import attention as A
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
     G = H // cfg.get("Hkv", H)
     heads = 0
-    t0 = time.perf_counter()
-    while heads < B * H:
-        b, h = divmod(heads, H)
-        A.head_backward(inp["q"][b, h], inp["k"][b, h // G], inp["v"][b, h // G], inp["do"][b, h], scale,
-                        cfg["causal"], **oracle_mask(cfg))
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    with pinned_blas() as pin:
+        threads = pin.cores
+        t0 = time.perf_counter()
+        while heads < B * H:
+            b, h = divmod(heads, H)
+            A.head_backward(inp["q"][b, h], inp["k"][b, h // G], inp["v"][b, h // G], inp["do"][b, h], scale,
+                            cfg["causal"], **oracle_mask(cfg))
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
     f_fwd, f_bwd = workload_flops(dict(cfg, B=1, H=1))
     per_head = dt / heads
     return {
@@ -400,13 +435,13 @@ def run_prep(args, cfg):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         from oracle import attention as A
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         o_h = o.float().cpu().numpy()
-        t0 = time.perf_counter()
-        A.preprocess_d(o_h, inp["do"])
-        dt = time.perf_counter() - t0
+        with pinned_blas() as pin:
+            threads = pin.cores
+            t0 = time.perf_counter()
+            A.preprocess_d(o_h, inp["do"])
+            dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
                                   "kind": "oracle", "sample": f"the whole step (all {B * H * N} rows, fp64) "
                                                               f"in {dt:.2f} s"}
@@ -468,14 +503,208 @@ def run_decode(args, cfg):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         from oracle import decode as Dc
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        t0 = time.perf_counter()
-        Dc.decode_forward(inp["q"], inp["k"], inp["v"], scale)
-        dt = time.perf_counter() - t0
+        with pinned_blas() as pin:
+            threads = pin.cores
+            t0 = time.perf_counter()
+            Dc.decode_forward(inp["q"], inp["k"], inp["v"], scale)
+            dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
                                   "kind": "oracle", "sample": f"the whole step (all {B * H} heads) in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_varlen(args, cfg):
+    """Packed variable-length sequences with a key-padding mask: one step is
+    attn_fwd_varlen then attn_bwd_varlen (its dQ pass, which also forms D, and
+    its dK/dV pass).  FLOPs are the dense formulas summed per sequence (N =
+    L_s).  The events bracket the forward and the whole backward; the
+    roofline object is the forward kernel (the launch bracketed alone)."""
+    import numpy as np
+    import torch
+    import exact_tiled_attention_09_amd as M
+    from attn_inputs import left_padding_key_mask, varlen_inputs
+    H, d, causal = cfg["H"], cfg["d"], cfg["causal"]
+    scale = 1.0 / math.sqrt(d)
+    log(f"workload {args.workload}: generating inputs")
+    inp = varlen_inputs(cfg["nseq"], cfg["len_lo"], cfg["len_hi"], H, d, "bf16", seed=0)
+    cu = inp["cu_seqlens"]
+    kv = left_padding_key_mask(cu, cfg["pad"])
+    T, maxlen = int(cu[-1]), int(inp["max_seqlen"])
+    q, k, v, do = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda().contiguous() for n in ("q", "k", "v", "do"))
+    cu_d = torch.from_numpy(cu).cuda()
+    kv_d = torch.from_numpy(kv).cuda()
+    M.check_cu_seqlens(cu, T, maxlen, "bench")
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(M.attn_bwd_varlen_workspace_bytes(T, H, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.attn_fwd_varlen(q, k, v, o, lse, cu_d, maxlen, scale, causal, kv_d, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_d, maxlen, scale, causal, ws, kv_d, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    with no_gc():
+        t0 = time.perf_counter()
+        for ev in events:
+            step(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    f_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
+    b_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
+    lengths = np.diff(cu).astype(np.float64)
+    f_fwd = float(np.sum(4.0 * H * lengths ** 2 * d * (0.5 if causal else 1.0)))
+    f_bwd = 2.5 * f_fwd
+    ms_step = wall * 1e3 / args.steps
+    tf_fwd = f_fwd / (f_ms * 1e-3) / 1e12
+    tf_bwd = f_bwd / (b_ms * 1e-3) / 1e12
+    by = kernel_bytes(1, H, H, T, d)
+    label = "fwd_stag_kernel (attn_fwd_varlen, packed, key padding)"
+    roofline = roofline_entry(label, f_ms, f_fwd, by["fwd"] + T, None)
+    dead = sum(int(np.sum(np.cumsum(kv[cu[i]:cu[i + 1]]) == 0)) for i in range(len(cu) - 1))
+    result = {
+        "metric": f"attn fwd+bwd TFLOPS, {args.workload}, 1 MI355X",
+        "value": round((f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"exact attention fwd+bwd, packed {len(lengths)} sequences (lengths uniform in "
+                               f"[{cfg['len_lo']}, {cfg['len_hi']}], seed 0, {T} tokens), "
+                               f"{'causal' if causal else 'non-causal'}, left key padding "
+                               f"({dead} fully masked rows), H{H} d{d} bf16",
+                   "nseq": len(lengths), "total_tokens": T, "max_seqlen": maxlen, "H": H, "d": d,
+                   "causal": causal, "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd,
+                   "fully_masked_rows_per_head": dead},
+        "fwd": {"ms": round(f_ms, 4), "tflops": round(tf_fwd, 2),
+                "pct_mfma_peak": round(100 * tf_fwd / PEAK_BF16_TFLOPS, 2)},
+        "bwd": {"ms": round(b_ms, 4), "tflops": round(tf_bwd, 2),
+                "pct_mfma_peak": round(100 * tf_bwd / PEAK_BF16_TFLOPS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one head over every sequence")
+        from oracle import attention as A
+        with pinned_blas() as pin:
+            t0 = time.perf_counter()
+            A.varlen_backward(inp["q"], inp["k"], inp["v"], inp["do"], cu, scale, causal, kv, heads=[0])
+            dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round((f_fwd + f_bwd) / H / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(pin.cores),
+            "kind": "oracle",
+            "sample": f"head 0 over all {len(lengths)} sequences (fp64, forward+backward) in {dt:.1f} s on the "
+                      f"host; whole-job time scales by H: {dt * H:.0f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_f32(args, cfg):
+    """The fp32 problem: one step is attn_fwd_f32 then attn_bwd_f32.  At 4.2
+    MFLOP it is latency-bound (a handful of workgroups), so the line reports
+    its time; its parity against the oracle is measured in the CPU-baseline
+    leg, which runs the oracle on the same inputs anyway."""
+    import numpy as np
+    import torch
+    import exact_tiled_attention_09_amd as M
+    from attn_inputs import dense_inputs
+    B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
+    scale = 1.0 / math.sqrt(d)
+    inp = dense_inputs(B, H, N, d, "f32", seed=0)
+    q, k, v, do = (torch.from_numpy(inp[n]).cuda().contiguous() for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(M.attn_bwd_f32_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.attn_fwd_f32(q, k, v, o, lse, scale, causal, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    with no_gc():
+        t0 = time.perf_counter()
+        for ev in events:
+            step(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    f_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
+    b_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
+    f_fwd, f_bwd = flops(B, H, N, d, causal)
+    ms_step = wall * 1e3 / args.steps
+    tf = f_fwd / (f_ms * 1e-3) / 1e12
+    result = {
+        "metric": f"attn fwd+bwd time, {args.workload}, 1 MI355X",
+        "value": round(ms_step * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"exact attention fwd+bwd fp32, {'causal' if causal else 'non-causal'} "
+                               f"B{B} H{H} N{N} d{d}", "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd},
+        "fwd": {"us": round(f_ms * 1e3, 2)},
+        "bwd": {"us": round(b_ms * 1e3, 2)},
+        "roofline": {"kernel": "fwd_f32_kernel (attn_fwd_f32)", "bound": "mfma", "achieved": round(tf, 4),
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 6),
+                     "traffic": None, "flops_per_launch": f_fwd, "avg_launch_ms": round(f_ms, 5),
+                     "note": "latency-bound: 4 workgroups of 32 query rows on a 256-CU chip"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import attention as A
+        with pinned_blas() as pin:
+            t0 = time.perf_counter()
+            reps = 0
+            while True:
+                ref = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal)
+                reps += 1
+                if time.perf_counter() - t0 >= 1.0:
+                    break
+            dt = (time.perf_counter() - t0) / reps
+        got = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+        err = {n: float(np.max(np.abs(t.cpu().numpy().astype(np.float64) - ref[n]))) for n, t in got.items()}
+        result["cpu_baseline"] = {
+            "value": round(dt * 1e6, 1), "unit": "us/step", "cores": int(pin.cores), "kind": "oracle",
+            "sample": f"the whole step (fp64, forward+backward), mean of {reps} runs",
+            "max_abs_err_gpu_vs_oracle": {n: float(f"{e:.3e}") for n, e in err.items()},
+            "parity_bar": 1e-5}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -487,7 +716,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT,
                     choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS) + sorted(FP8_WORKLOADS)
-                    + sorted(PREP_WORKLOADS))
+                    + sorted(PREP_WORKLOADS) + sorted(VARLEN_WORKLOADS) + sorted(F32_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; its FETCH_SIZE / "
@@ -526,6 +755,10 @@ def main(argv=None):
         return run_fp8(args, FP8_WORKLOADS[args.workload])
     if args.workload in PREP_WORKLOADS:
         return run_prep(args, PREP_WORKLOADS[args.workload])
+    if args.workload in VARLEN_WORKLOADS:
+        return run_varlen(args, VARLEN_WORKLOADS[args.workload])
+    if args.workload in F32_WORKLOADS:
+        return run_f32(args, F32_WORKLOADS[args.workload])
 
     cfg = WORKLOADS[args.workload]
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]

@@ -87,3 +87,21 @@ def test_cli_refuses_several_gpus_and_bad_counts(capsys):
     assert "one GPU only" in capsys.readouterr().err
     assert bench.main(["--steps", "0"]) == 2
     assert bench.main(["--warmup", "-1"]) == 2
+
+
+def test_cpu_baseline_cores_are_the_affinity_set():
+    """The CPU baseline reports the cores of this process's affinity set and
+    runs the oracle's BLAS with exactly that many threads."""
+    import os
+
+    from threadpoolctl import threadpool_info
+    assert bench.host_cores() == len(os.sched_getaffinity(0))
+    with bench.pinned_blas() as pin:
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        assert pin.cores == len(os.sched_getaffinity(0))
+        assert all(p["num_threads"] == pin.cores for p in blas)
+
+
+def test_new_workloads_are_listed():
+    assert "varlen_causal_keypad_h32_d128" in bench.VARLEN_WORKLOADS
+    assert "f32_b1_h1_n128_d64" in bench.F32_WORKLOADS
