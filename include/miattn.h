@@ -50,7 +50,17 @@
  *   MIATTN_ERR_UNSUPPORTED  head dim d is not 64 or 128;
  *   MIATTN_ERR_HIP          a kernel launch was rejected by the runtime.
  * The contents of cu_seqlens and key_valid live on the device and are not
- * checked; offsets that break the contract above are undefined behaviour.
+ * checked on the host (the binding's check_cu_seqlens checks a host copy);
+ * the kernels clamp offsets into [0, total_tokens] and lengths to
+ * max_seqlen, so offsets that break the contract above give unspecified
+ * results but never address memory outside the tensors.
+ *
+ * Non-finite inputs are ordinary inputs: a NaN or Inf in Q, K, V or dO makes
+ * NaN of what depends on it and never faults.  A query row whose scores hold
+ * a NaN or an Inf gets NaN in its O and LSE (other rows are unaffected).  In
+ * the backward, masked pairs enter the matrix products as exact zeros and
+ * 0 * Inf = NaN, so a non-finite query row also turns NaN the dK, dV of the
+ * keys that share a backward tile (at most 128 keys) with it.
  * Calls that overlap on one stream are ordered; calls on different streams
  * that share output or workspace buffers race.
  */

@@ -116,10 +116,37 @@ def map_heads(fn, jobs):
             return list(ex.map(fn, jobs))
 
 
-def sample_positions(n: int, count: int, rng) -> np.ndarray:
-    """`count` distinct positions of [0, n) including the first two and the
-    last two, the rest drawn by rng; sorted."""
+def sample_positions(n: int, count: int, rng):
+    """`count` distinct positions of [0, n): the first two and the last two,
+    the rest drawn uniformly by rng; sorted.  Returns (positions, weights):
+    a fixed position stands for itself (weight 1), a drawn one for its share
+    of the positions not fixed, so weighted sums over the sample estimate
+    sums over all n positions without bias."""
     fixed = sorted({0, 1, n - 2, n - 1} & set(range(n)))
     rest = np.setdiff1d(np.arange(n), fixed)
     extra = rng.choice(rest, size=min(len(rest), max(0, count - len(fixed))), replace=False)
-    return np.sort(np.concatenate([np.asarray(fixed, np.int64), extra.astype(np.int64)]))
+    pos = np.concatenate([np.asarray(fixed, np.int64), extra.astype(np.int64)])
+    w = np.concatenate([np.ones(len(fixed)), np.full(len(extra), len(rest) / max(1, len(extra)))])
+    order = np.argsort(pos)
+    return pos[order], w[order]
+
+
+def check_bf16_sampled(gpu, ref, weights, what):
+    """The bf16 relative Frobenius bar on sampled rows: the whole tensor's
+    ||gpu - ref|| / ||ref||, estimated from the rows with their sample
+    weights (sample_positions).  Returns (estimate, worst single-row relative
+    error) -- the latter is a diagnostic: a row that sees only a couple of keys
+    can carry a few percent of bf16 rounding on its own without breaking the
+    tensor-wide bar."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    w = np.asarray(weights, np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    e2 = np.sum((g - r) ** 2, axis=1)
+    r2 = np.sum(r ** 2, axis=1)
+    den = float(np.sum(w * r2))
+    est = float(np.sqrt(np.sum(w * e2) / den)) if den > 0 else float(np.sqrt(np.sum(w * e2)))
+    assert est <= BF16_REL_FRO, f"{what}: estimated relative Frobenius error {est:.3e} > {BF16_REL_FRO:.0e}"
+    rows = r2 > 0
+    worst = float(np.max(np.sqrt(e2[rows] / r2[rows]))) if np.any(rows) else 0.0
+    return est, worst

@@ -9,7 +9,10 @@ Every head of every configuration is compared with the fp64 oracle:
     LSE of every row of the head, dQ at 32 query rows and dK, dV at 32 key
     columns (always including the first two and last two of the head);
     packed sequences: 8 rows and 8 key columns of every sequence of every
-    head.
+    head.  The gradients' bar, a relative Frobenius error over the whole
+    tensor, is applied to its estimate from the sample (each drawn row
+    weighted by the share of the head it stands for); the worst single row
+    is printed beside it.
 Properties that hold at any size are checked too: finite outputs, the -inf
 pattern of LSE, and for causal problems the first row of every head (it sees
 one key: O_0 = V_0 exactly, LSE_0 = scale * q_0 . k_0).  The oracle work runs
@@ -22,8 +25,8 @@ import pytest
 
 from attn_inputs import dense_inputs, left_padding_key_mask, varlen_inputs
 from oracle import attention as A
-from parity_utils import (BF16_O_MAX_ABS, LSE_MAX_ABS, check_bf16, check_f32, check_lse, map_heads,
-                          sample_positions, tile_rel_fro_max, to_dev, to_np)
+from parity_utils import (BF16_O_MAX_ABS, LSE_MAX_ABS, check_bf16, check_bf16_sampled, check_f32, check_lse,
+                          map_heads, sample_positions, tile_rel_fro_max, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,15 +105,14 @@ def _host_outputs(out):
 def _sampled_dense_head(job):
     """One head against head_backward_sampled: O and LSE of every row, dQ at
     the sampled rows, dK and dV at the sampled key columns."""
-    label, q, k, v, do, scale, causal, rows, cols, g = job
+    label, q, k, v, do, scale, causal, (rows, rw), (cols, cw), g = job
     dq, dk, dv, o, lse, _ = A.head_backward_sampled(q, k, v, do, scale, causal, None, rows, cols)
     fo, _ = check_bf16(g["o"], o, f"O{label}", max_abs_tol=BF16_O_MAX_ABS)
     check_lse(g["lse"], lse, what=f"LSE{label}")
     res = {"o": fo, "o_tile": tile_rel_fro_max(g["o"], o)}
-    if dq is not None and "dq" in g:
-        res["dq"] = check_bf16(g["dq"], dq, f"dq{label} rows")[0]
-        res["dk"] = check_bf16(g["dk"], dk, f"dk{label} cols")[0]
-        res["dv"] = check_bf16(g["dv"], dv, f"dv{label} cols")[0]
+    if len(rows):
+        for name, got, ref, w in (("dq", g["dq"], dq, rw), ("dk", g["dk"], dk, cw), ("dv", g["dv"], dv, cw)):
+            res[name], res[name + "_row"] = check_bf16_sampled(got, ref, w, f"{name}{label}")
     return res
 
 
@@ -124,10 +126,11 @@ def _every_head(inp, outh, scale, causal, heads, bwd, seed):
         cols = sample_positions(N, 32, rng)
         g = {"o": outh["o"][b, h], "lse": outh["lse"][b, h]}
         if bwd:
-            g.update(dq=outh["dq"][b, h][rows], dk=outh["dk"][b, h][cols], dv=outh["dv"][b, h][cols])
+            g.update(dq=outh["dq"][b, h][rows[0]], dk=outh["dk"][b, h][cols[0]], dv=outh["dv"][b, h][cols[0]])
+        none = (np.zeros(0, np.int64), np.zeros(0))
         jobs.append((f"[{b},{h}]", inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
                      inp["do"][b, h] if bwd else inp["q"][b, h], scale, causal,
-                     rows if bwd else [], cols if bwd else [], g))
+                     rows if bwd else none, cols if bwd else none, g))
     res = map_heads(_sampled_dense_head, jobs)
     worst = {key: max(r[key] for r in res) for key in res[0]}
     _say(f"  {len(heads)} heads sampled; worst rel-fro " + ", ".join(f"{k_} {v_:.2e}" for k_, v_ in worst.items()))
@@ -306,25 +309,28 @@ def _sampled_packed_head(job):
     h, inp, kv, out, scale = job
     cu = inp["cu_seqlens"]
     rng = np.random.default_rng(5000 + h)
-    acc = {n: ([], []) for n in ("o", "dq", "dk", "dv")}
+    acc = {n: ([], [], []) for n in ("dq", "dk", "dv")}
+    og, orf = [], []
     for s in range(len(cu) - 1):
         t0, t1 = int(cu[s]), int(cu[s + 1])
         L = t1 - t0
-        rows = sample_positions(L, 8, rng)
-        cols = sample_positions(L, 8, rng)
+        rows, rw = sample_positions(L, 8, rng)
+        cols, cw = sample_positions(L, 8, rng)
         sl = slice(t0, t1)
         dq, dk, dv, o, lse, _ = A.head_backward_sampled(inp["q"][sl, h], inp["k"][sl, h], inp["v"][sl, h],
                                                         inp["do"][sl, h], scale, True, kv[sl], rows, cols)
         check_lse(out["lse"][h, sl], lse, what=f"LSE[seq {s}, head {h}]")
-        for name, got, ref in (("o", out["o"][sl, h], o), ("dq", out["dq"][sl, h][rows], dq),
-                               ("dk", out["dk"][sl, h][cols], dk), ("dv", out["dv"][sl, h][cols], dv)):
+        og.append(out["o"][sl, h])
+        orf.append(o)
+        for name, got, ref, w in (("dq", out["dq"][sl, h][rows], dq, rw), ("dk", out["dk"][sl, h][cols], dk, cw),
+                                  ("dv", out["dv"][sl, h][cols], dv, cw)):
             acc[name][0].append(got)
             acc[name][1].append(ref)
-    res = {}
-    for name, (gs, rs) in acc.items():
-        g, r = np.concatenate(gs), np.concatenate(rs)
-        res[name] = check_bf16(g, r, f"{name}[head {h}] samples",
-                               max_abs_tol=BF16_O_MAX_ABS if name == "o" else None)[0]
+            acc[name][2].append(w)
+    res = {"o": check_bf16(np.concatenate(og), np.concatenate(orf), f"O[head {h}]", max_abs_tol=BF16_O_MAX_ABS)[0]}
+    for name, (gs, rs, ws) in acc.items():
+        res[name], res[name + "_row"] = check_bf16_sampled(np.concatenate(gs), np.concatenate(rs),
+                                                           np.concatenate(ws), f"{name}[head {h}] samples")
     return res
 
 
