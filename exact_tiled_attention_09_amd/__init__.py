@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     attn_bwd_f32,
     attn_bwd_f32_workspace_bytes,
     attn_bwd_gqa,
+    attn_bwd_noalloc,
+    attn_bwd_noalloc_max_rows,
     attn_bwd_block_sparse,
     attn_bwd_block_sparse_workspace_bytes,
     attn_bwd_window,

@@ -18,6 +18,7 @@ MIATTN_OK = 0
 MIATTN_ERR_INVALID_ARG = -1
 MIATTN_ERR_UNSUPPORTED = -2
 MIATTN_ERR_HIP = -3
+MIATTN_ERR_TOO_LARGE = -4
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -32,6 +33,8 @@ SIGNATURES = {
     "attn_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_bwd_f32_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_noalloc_max_rows": (_S, []),
     "attn_bwd_preprocess": (_I, [_P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "attn_bwd_dkdv": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_bwd_dq": (_I, [_P] * 6 + [_I, _I, _I, _I, _F, _I, _P, _S, _P]),
@@ -170,6 +173,22 @@ def attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, worksp
                                        _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
+
+
+def attn_bwd_noalloc_max_rows() -> int:
+    return int(load().attn_bwd_noalloc_max_rows())
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, scale: float, causal: bool, stream=None):
+    """attn_bwd without a workspace: D lives in the library's own device
+    scratch (B*H*N <= attn_bwd_noalloc_max_rows()); calls overlapping on one
+    GPU race."""
+    B, H, N, d = _dense_dims(q)
+    _dense_specs("attn_bwd_noalloc", "bfloat16", B, H, N, d, q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk,
+                 dv=dv)
+    _check("attn_bwd_noalloc", load().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                                                       int(bool(causal)), _stream(stream)))
 
 
 def attn_bwd_preprocess(o, dO, workspace, stream=None):

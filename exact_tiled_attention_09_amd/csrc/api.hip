@@ -1,6 +1,7 @@
 // C-ABI layer of libmiattn: argument validation, workspace carving and
 // dispatch to the gfx950 kernels.  Nothing here allocates, frees or
 // synchronises; every launch goes to the caller's stream.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -160,6 +161,29 @@ SparsePlan sparse_plan(int B, int H, int H_kv, int N, int d, int nnz) {
   return p;
 }
 
+// Scratch of the allocation-free backward (attn_bwd_noalloc): D for every
+// row, in a file-scope device array that each GPU holds from the library's
+// load until the process ends.  In host code `scratch` only names the symbol;
+// its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and kept in scratch_ptr.  Every call on one GPU shares
+// that GPU's copy, so calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = (size_t)32 << 20;   // D of up to 8M rows
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch, or nullptr on a HIP error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 AttnArgs dense_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
                     int N, float scale) {
   AttnArgs a = {};
@@ -190,6 +214,7 @@ const char* miattn_status_string(int status) {
     case MIATTN_ERR_INVALID_ARG: return "invalid argument";
     case MIATTN_ERR_UNSUPPORTED: return "unsupported head dimension (supported: 64, 128)";
     case MIATTN_ERR_HIP: return "HIP runtime error at launch";
+    case MIATTN_ERR_TOO_LARGE: return "problem larger than the library's built-in scratch (attn_bwd_noalloc: B*H*N <= 8388608)";
     default: return "unknown status";
   }
 }
@@ -289,6 +314,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.dv = dv;
   carve(a, workspace, rows);
   // the dQ pass computes and stores D (no pre-pass); the dK/dV pass reads it
+  a.dq_writes_d = 1;
+  if (int st = hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream))) return st;
+  return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream));
+}
+
+size_t attn_bwd_noalloc_max_rows(void) { return kScratchBytes / sizeof(float); }
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                     void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                     hipStream_t stream) {
+  if (!ptr16(q) || !ptr16(k) || !ptr16(v) || !ptr16(o) || !ptr16(lse) || !ptr16(dO) || !ptr16(dq) ||
+      !ptr16(dk) || !ptr16(dv))
+    return MIATTN_ERR_INVALID_ARG;
+  if (int st = check_dense(B, H, N, d, scale)) return st;
+  const int64_t rows = (int64_t)B * H * N;
+  if ((size_t)rows > kScratchBytes / sizeof(float)) return MIATTN_ERR_TOO_LARGE;
+  void* ws = device_scratch();
+  if (ws == nullptr) return MIATTN_ERR_HIP;
+  AttnArgs a = dense_args(q, k, v, o, lse, B, H, N, scale);
+  a.dout = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  carve(a, ws, rows);
+  // the same two passes as attn_bwd: the dQ pass writes D of every row into
+  // the scratch before the dK/dV pass reads it, so nothing needs clearing
   a.dq_writes_d = 1;
   if (int st = hip_status(miattn::launch_bwd_dq_bf16(a, d, causal != 0, false, stream))) return st;
   return hip_status(miattn::launch_bwd_dkdv_bf16(a, d, causal != 0, false, stream));

@@ -78,6 +78,7 @@ extern "C" {
 #define MIATTN_ERR_INVALID_ARG (-1)
 #define MIATTN_ERR_UNSUPPORTED (-2)
 #define MIATTN_ERR_HIP (-3)
+#define MIATTN_ERR_TOO_LARGE (-4)
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int miattn_version(void);
@@ -115,6 +116,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dO, void* dq, void* dk, void* dv,
              int B, int H, int N, int d, float scale, int causal,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Allocation-free form of attn_bwd, for callers that cannot allocate device
+ * memory or pass a workspace (code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, kernels and
+ * result (bit for bit) as attn_bwd without the workspace: D lives in a
+ * scratch array built into the library, 32 MiB of device memory per GPU,
+ * held from the library's load until the process ends.  Limit: B*H*N <=
+ * attn_bwd_noalloc_max_rows() (8388608); larger problems return
+ * MIATTN_ERR_TOO_LARGE before any launch.  Calls no allocating routine.  All
+ * calls on one GPU share its scratch: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * The first call on a device looks up the scratch's address on it (a HIP
+ * error there returns MIATTN_ERR_HIP). */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv,
+                     int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+size_t attn_bwd_noalloc_max_rows(void);
 
 /* The D pre-pass, stage 1 of the three-stage backward (attn_bwd itself forms
  * D inside its dQ pass, attn_bwd_dq_preprocess): D = rowsum(dO o O) in fp32

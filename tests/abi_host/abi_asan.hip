@@ -119,6 +119,10 @@ int main() {
   CHECK(attn_decode(q.p, k.p, v.p, o.p, (float*)lse.p, B, H, 3, N, d, sc, nullptr, q.p, 1 << 20, 0) ==
         MIATTN_ERR_INVALID_ARG);
   CHECK(attn_quantize_fp8_rows(q.p, (unsigned char*)o.p, (float*)lse.p, B, H, N, 64, 0) == MIATTN_ERR_UNSUPPORTED);
+  CHECK(attn_bwd_noalloc(q.p, k.p, v.p, o.p, (float*)lse.p, g.p, dq.p, dk.p, dv.p, 1, 1,
+                         (int)attn_bwd_noalloc_max_rows() + 1, 64, sc, 1, 0) == MIATTN_ERR_TOO_LARGE);
+  CHECK(attn_bwd_noalloc(q.p, k.p, v.p, o.p, nullptr, g.p, dq.p, dk.p, dv.p, B, H, N, d, sc, 1, 0) ==
+        MIATTN_ERR_INVALID_ARG);
   CHECK(g_launches == before);
 
   // ---- valid calls: launched once per stage, workspace carved inside its buffer
@@ -169,7 +173,7 @@ int main() {
                        (float*)dk.p, (float*)dv.p, B, H, N, 64, sc, 0, ws.p, wsb, 0) == MIATTN_OK);
     CHECK(inside(g_last.dvec, ws, R) && inside(g_last.dq_acc, ws, (size_t)B * H * N * 64 * 4));
   }
-  for (int st : {MIATTN_OK, MIATTN_ERR_INVALID_ARG, MIATTN_ERR_UNSUPPORTED, MIATTN_ERR_HIP, 12345})
+  for (int st : {MIATTN_OK, MIATTN_ERR_INVALID_ARG, MIATTN_ERR_UNSUPPORTED, MIATTN_ERR_HIP, MIATTN_ERR_TOO_LARGE, 12345})
     CHECK(miattn_status_string(st) != nullptr && std::strlen(miattn_status_string(st)) > 0);
 
   if (g_fail) {
