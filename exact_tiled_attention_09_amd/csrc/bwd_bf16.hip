@@ -116,7 +116,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     kt = item & 0xffff;
     chunk = item >> 16;
   } else {
-    wg_coords(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);  // the earliest key tiles carry the most work
+    // the earliest key tiles carry the most work; packed sequences go
+    // tile-major over every (sequence, head) so that their very different
+    // lengths spread over the XCDs
+    if (VARLEN) wg_coords_tile_major(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);
+    else wg_coords(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);
   }
   const int G = a.H / a.Hkv;
   const int b = bh / a.Hkv;
@@ -509,7 +513,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   // causal masks, windows and block lists: groups of four heads per XCD,
   // heaviest tiles first in each group under a causal mask; plain non-causal:
   // all heads' tile 0, then all tile 1, ... (measured faster there)
-  if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
+  // packed sequences: tile-major over every (sequence, head), heaviest first
+  // (as the forward), so sequences of very different lengths spread over XCDs
+  if (VARLEN) wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);
+  else if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;

@@ -73,7 +73,11 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   // causal masks, windows and block lists: groups of four heads per XCD,
   // heaviest tiles first in each group under a causal mask; plain non-causal:
   // all heads' tile 0, then all tile 1, ... (measured faster there)
-  if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
+  // packed sequences: every (sequence, head)'s tile t together, heaviest
+  // tiles first, so that sequences of very different lengths spread over
+  // all XCDs (a contiguous range per XCD would give one XCD the longest ones)
+  if (VARLEN) wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);
+  else if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
