@@ -20,11 +20,13 @@
 //    per tile) in the XOR-swizzled layout of swz<D>, which keeps both the b128
 //    operand reads and the transpose reads free of bank conflicts; Q stays in
 //    registers for the whole key loop.
-//  * softmax runs in base 2 with scale * log2(e) folded into one FMA.  A row's
-//    reference max is only raised when a tile's max exceeds it by more than
-//    kLazyMax (base-2 units); below that the stale reference is kept, P~ stays
-//    below 2^kLazyMax, and O~ and l need no rescale.  Any reference value gives
-//    the same O = O~ / l and LSE = m + log2 l, so this changes only rounding.
+//  * softmax runs in base 2 with scale * log2(e) folded into one FMA.  A tile
+//    is first exponentiated against the row's current reference without
+//    forming the row max; only when a partial row sum exceeds 2^16 (or the row
+//    has no reference yet) is the max taken and the reference raised (when
+//    the max exceeds it by more than kLazyMax, base-2 units), O~ and l
+//    rescaled and the tile redone.  Any reference value gives the same
+//    O = O~ / l and LSE = m + log2 l, so this changes only rounding.
 //  * causal: key tiles above the diagonal are never loaded; only tiles that
 //    cross the diagonal, the sequence end or a padded key are masked
 //    element-wise; each XCD takes its heads four at a time, their query tiles heaviest first (wg_coords_grouped);
@@ -267,58 +269,80 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
       // Scale first, then hide masked entries as -inf; afterwards the
       // exponent uses multiplier 1 (so scale == 0 cannot make 0 * -inf).
       cc = 1.f;
-      const int qi = pin_in_branch(q_wave0 + l32);
+      if constexpr (!KPAD && MASK != kMaskWindow) {
+        // sequence end and causal diagonal only: entry r of key block kb
+        // holds key kt0 + kb*32 + (r/4)*8 + hi*4 + r%4, visible iff its
+        // offset kb*32 + (r/4)*8 + r%4 is at most this lane's bound
+        int lim = kv_len - 1 - kt0 - hi * 4;
+        if (CAUSAL) lim = min(lim, q_wave0 + l32 - kt0 - hi * 4);
+        lim = pin_in_branch(lim);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = (kb * 32 + (r >> 2) * 8 + (r & 3) <= lim) ? s[kb][r] * c : kNegInf;
+      } else {
+        const int qi = pin_in_branch(q_wave0 + l32);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            const int key = kt0 + kl;
+            bool vis = key < kv_len;
+            if (CAUSAL) vis = vis && key <= qi;
+            if (KPAD) vis = vis && s_valid[j & 3][kl] != 0;
+            if (MASK == kMaskWindow) vis = vis && key >= qi - a.win_left && key <= qi + a.win_right;
+            s[kb][r] = vis ? s[kb][r] * c : kNegInf;
+          }
+      }
+    }
+    auto expo = [&](float mu) __attribute__((always_inline)) -> float {
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          const int key = kt0 + kl;
-          bool vis = key < kv_len;
-          if (CAUSAL) vis = vis && key <= qi;
-          if (KPAD) vis = vis && s_valid[j & 3][kl] != 0;
-          if (MASK == kMaskWindow) vis = vis && key >= qi - a.win_left && key <= qi + a.win_right;
-          s[kb][r] = vis ? s[kb][r] * c : kNegInf;
+        for (int t = 0; t < 2; ++t) {
+          float e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            e[i] = fast_exp2(__builtin_fmaf(s[kb][8 * t + i], cc, -mu));
+            rs += e[i];
+          }
+          p[kb * 2 + t] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
         }
-    }
-    float mx = kNegInf;
+      return rs;
+    };
+    // P against the current reference first, without the row max.  Only
+    // when a lane's partial row sum leaves (0, 2^16] -- the row's scores rose
+    // well above the reference, a NaN or Inf score, or no reference yet
+    // (m = -inf) -- does the wave take the row max, move the reference (when
+    // the max exceeds it by more than kLazyMax), rescale and redo the tile.
+    // Any reference gives the same O = O~ / l and LSE = m + log2 l; this one
+    // only keeps every P below 2^16.
+    float rs = expo(m == kNegInf ? 0.f : m);
+    if (wave_any(!(rs <= kSumLimit) || m == kNegInf)) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx *= cc;
-    // The reference of a row moves only when the tile's row max exceeds it by
-    // more than kLazyMax.  While no lane's half of a row does, the wave skips
-    // the exchange between halves and the rescale (the common case after the
-    // first tiles); a row with no reference yet (m = -inf) and a visible key
-    // always takes the update.
-    if (wave_any(!(mx <= m + kLazyMax))) {
-      mx = wave_max_halves(mx);
-      const float m_new = (mx > m + kLazyMax) ? mx : m;
-      const bool dead = m_new == kNegInf;  // no visible key yet for this row
-      const float alpha = dead ? 1.f : fast_exp2(m - m_new);
-      l *= alpha;
-      m = m_new;
-      if (wave_any(alpha != 1.f)) {
-        const float a_ = pin_in_branch(alpha);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx *= cc;
+      if (wave_any(!(mx <= m + kLazyMax))) {
+        mx = wave_max_halves(mx);
+        const float m_new = (mx > m + kLazyMax) ? mx : m;
+        const bool dead = m_new == kNegInf;
+        const float alpha = dead ? 1.f : fast_exp2(m - m_new);
+        l *= alpha;
+        m = m_new;
+        if (wave_any(alpha != 1.f)) {
+          const float a_ = pin_in_branch(alpha);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= a_;
-      }
-    }
-    const float mu = m == kNegInf ? 0.f : m;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          e[i] = fast_exp2(__builtin_fmaf(s[kb][8 * t + i], cc, -mu));
-          rs += e[i];
+          for (int db = 0; db < DB; ++db) o[db] *= a_;
         }
-        p[kb * 2 + t] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       }
+      rs = expo(m == kNegInf ? 0.f : m);
+    }
     l += rs;
   };
 

@@ -38,6 +38,9 @@ constexpr float kPosInf = __builtin_huge_valf();
 // when a tile's max exceeds it by more than this (base-2 units), so P~ stays
 // below 2^kLazyMax; any reference gives the same O and LSE up to rounding.
 constexpr float kLazyMax = 8.0f;
+// The forward exponentiates a tile against the running reference without the
+// row max while every partial row sum stays at or below this (so every P~ does).
+constexpr float kSumLimit = 65536.0f;
 
 // Everything a kernel needs to address one problem.  Dense tensors are
 // [B, H, N, d] with LSE/D as [B, H, N]; packed tensors are [T, H, d] with
