@@ -943,24 +943,34 @@ __global__ void __launch_bounds__(256) block_table_kernel(AttnArgs a, uint8_t* t
   }
 }
 
-// The balanced work list of the key-tile pass (one workgroup of 64
+// The balanced work list of the key-tile pass (one workgroup of 1024
 // threads): per key block the length of its query list (the same causal
-// filter as build_query_block_list), its chunk count, the work items and the
-// partial-sum slots of the blocks that are cut.  The chunks of cut blocks
-// (the longest items) come first in the list, so that none of them starts
-// last.
-__global__ void __launch_bounds__(64) block_work_kernel(AttnArgs a, int causal, int* work, int* slot, int* nch) {
-  const int lane = threadIdx.x;
+// filter as build_query_block_list), counted in parallel over the expanded
+// table with LDS integer adds (exact, so the order does not matter); then one
+// wave places the work items and the partial-sum slots of the blocks that
+// are cut.  The chunks of cut blocks (the longest items) come first in the
+// list, so that none of them starts last.
+__global__ void __launch_bounds__(1024) block_work_kernel(AttnArgs a, int causal, int* work, int* slot, int* nch) {
+  __shared__ int s_count[kMaxSparseBlocks];
+  const int tid = threadIdx.x;
+  for (int c = tid; c < a.n_kblk; c += 1024) s_count[c] = 0;
+  __syncthreads();
+  const int total = a.n_qblk * a.n_kblk;
+  for (int idx = tid; idx < total; idx += 1024) {
+    const int r = idx / a.n_kblk;
+    const int c = idx - r * a.n_kblk;
+    if ((!causal || r >= c) && a.blk_table[idx] != 0) atomicAdd(&s_count[c], 1);
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
   // pass 0 places the chunks of cut blocks, pass 1 the uncut blocks
   int carry = 0;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     for (int base = 0; base < a.n_kblk; base += 64) {
       const int c = base + lane;
-      int count = 0;
-      if (c < a.n_kblk) {
-        for (int r = causal ? c : 0; r < a.n_qblk; ++r) count += a.blk_table[(int64_t)r * a.n_kblk + c] != 0;
-      }
+      const int count = c < a.n_kblk ? s_count[c] : 0;
       const int n = c < a.n_kblk ? max(1, (count + a.blk_chunk - 1) / a.blk_chunk) : 0;
       const int mine = (pass == 0) ? (n > 1 ? n : 0) : (n == 1 ? 1 : 0);
       int incl = mine;
@@ -970,14 +980,10 @@ __global__ void __launch_bounds__(64) block_work_kernel(AttnArgs a, int causal, 
         if (lane >= o) incl += t;
       }
       const int w0 = carry + incl - mine;   // exclusive position
-      if (mine > 0) {
-        for (int k = 0; k < mine; ++k) work[1 + w0 + k] = c | (k << 16);
-      }
-      if (c < a.n_kblk) {
-        if (pass == 0) {
-          nch[c] = n;
-          slot[c] = n > 1 ? w0 : -1;   // the cut blocks' items and slots share positions
-        }
+      for (int k = 0; k < mine; ++k) work[1 + w0 + k] = c | (k << 16);
+      if (c < a.n_kblk && pass == 0) {
+        nch[c] = n;
+        slot[c] = n > 1 ? w0 : -1;   // the cut blocks' items and slots share positions
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
@@ -986,42 +992,69 @@ __global__ void __launch_bounds__(64) block_work_kernel(AttnArgs a, int causal, 
 }
 
 // Sums the slots of each cut key block in chunk order and writes bf16 dK
-// (times scale) and dV; one workgroup per (batch, key/value head, key block).
+// (times scale) and dV.  One workgroup per (batch, key/value head, key
+// block, group of 16 keys); every thread adds 16-byte vectors of the fp32
+// partial sums chunk after chunk (the order of the sum per element is the
+// chunk order, as before) and writes 8-byte bf16 vectors.
 template <int D>
 __global__ void __launch_bounds__(256) block_reduce_kernel(AttnArgs a) {
   constexpr int BK = 128;
-  const int c = blockIdx.x % a.n_kblk;
-  const int bh = blockIdx.x / a.n_kblk;
+  constexpr int RG = 16;                      // keys per workgroup
+  constexpr int PER = RG * D / 4 / 256;       // 16-byte vectors per thread and tensor
+  static_assert(PER >= 1 && PER * 256 * 4 == RG * D, "whole vectors per thread");
+  const int g = blockIdx.x % (BK / RG);
+  const int rest = blockIdx.x / (BK / RG);
+  const int c = rest % a.n_kblk;
+  const int bh = rest / a.n_kblk;
   const int slot = a.blk_slot[c];
   if (slot < 0) return;
   const int n = a.blk_nch[c];
   const int b = bh / a.Hkv;
   const int hk = bh - b * a.Hkv;
   const int64_t kv_base = ((int64_t)b * a.Hkv + hk) * a.N * D;
-  const float* part = a.blk_part + ((int64_t)bh * a.blk_nslots + slot) * 2 * BK * D;
-  for (int e = threadIdx.x; e < BK * D; e += 256) {
-    const int kl = e / D;
-    const int key = c * BK + kl;
-    if (key >= a.N) break;
-    float sk = 0.f, sv = 0.f;
-    for (int t = 0; t < n; ++t) {
-      sk += part[(int64_t)t * 2 * BK * D + e];
-      sv += part[(int64_t)t * 2 * BK * D + BK * D + e];
+  const float* part = a.blk_part + ((int64_t)bh * a.blk_nslots + slot) * 2 * BK * D + g * RG * D;
+  f32x4 sk[PER], sv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    sk[i] = f32x4{};
+    sv[i] = f32x4{};
+  }
+  for (int t = 0; t < n; ++t) {
+    const float* pt = part + (int64_t)t * 2 * BK * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = 4 * ((int)threadIdx.x + i * 256);
+      const f32x4 xk = *(const f32x4*)(pt + e);
+      const f32x4 xv = *(const f32x4*)(pt + BK * D + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sk[i][u] += xk[u];
+        sv[i][u] += xv[u];
+      }
     }
-    const int64_t off = kv_base + (int64_t)key * D + (e - kl * D);
-    ((uint16_t*)a.dk)[off] = (uint16_t)(pack_bf16x2(sk * a.scale, 0.f) & 0xffffu);
-    ((uint16_t*)a.dv)[off] = (uint16_t)(pack_bf16x2(sv, 0.f) & 0xffffu);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = 4 * ((int)threadIdx.x + i * 256);
+    const int kl = g * RG + e / D;
+    const int key = c * BK + kl;
+    if (key < a.N) {
+      const int64_t off = kv_base + (int64_t)key * D + (e % D);
+      *(u32x2*)((uint16_t*)a.dk + off) = u32x2{pack_bf16x2(sk[i][0] * a.scale, sk[i][1] * a.scale),
+                                               pack_bf16x2(sk[i][2] * a.scale, sk[i][3] * a.scale)};
+      *(u32x2*)((uint16_t*)a.dv + off) = u32x2{pack_bf16x2(sv[i][0], sv[i][1]), pack_bf16x2(sv[i][2], sv[i][3])};
+    }
   }
 }
 
 hipError_t launch_block_work(const AttnArgs& a, bool causal, int* work, int* slot, int* nch, hipStream_t stream) {
   if (a.n_kblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL(block_work_kernel, dim3(1), dim3(64), 0, stream, a, causal ? 1 : 0, work, slot, nch);
+  hipLaunchKernelGGL(block_work_kernel, dim3(1), dim3(1024), 0, stream, a, causal ? 1 : 0, work, slot, nch);
   return hipGetLastError();
 }
 
 hipError_t launch_block_reduce(const AttnArgs& a, int d, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.B * a.Hkv * a.n_kblk;
+  const int64_t blocks = (int64_t)a.B * a.Hkv * a.n_kblk * (128 / 16);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (d == 128) hipLaunchKernelGGL(block_reduce_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
