@@ -68,8 +68,27 @@ def _compile(src: str, obj: str, verbose: bool) -> tuple[str, float]:
     return src, time.time() - t0
 
 
+PROBE_SRC = os.path.join(PKG, "calib", "mfma_probe.hip")
+PROBE = os.path.join(PKG, "calib", "mfma_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the standalone matrix-core calibration program (not part of the
+    library); returns its path."""
+    cmd = [hipcc(), *[f for f in COMMON_FLAGS if not f.startswith("-I") and f not in ("-fPIC", "-Wall")],
+           PROBE_SRC, "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for mfma_probe.hip:\n{res.stdout}\n{res.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every HIP source and link libmiattn.so; returns the library path."""
+    """Compile every HIP source and link libmiattn.so (and the calibration
+    program); returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
@@ -88,6 +107,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 
