@@ -198,6 +198,66 @@ def measured_traffic(kernel_label, workload):
     return int(k["hbm_read_bytes"] + k["hbm_write_bytes"])
 
 
+TRAFFIC_SOURCES = {"fwd_stag_kernel": ["fwd_bf16.hip", "miattn_device.h"],
+                   "bwd_dq_kernel": ["bwd_bf16.hip", "miattn_device.h"],
+                   "bwd_dkdv_kernel": ["bwd_bf16.hip", "miattn_device.h"],
+                   "bwd_prep_kernel": ["bwd_bf16.hip", "miattn_device.h"]}
+
+
+def _counter_means(csv_path, counter):
+    """Mean over dispatches of a rocprofv3 counter, per kernel name (the
+    counter's rows of one dispatch are summed first)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {name: sum(v) / len(v) for name, v in out.items()}
+
+
+def write_traffic_record(run_dir, workload, log_fn=print, out_path=None):
+    """profiles/traffic_<workload>.json from four rocprofv3 --pmc runs under
+    run_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of this workload's
+    bench.py run) and cal_fetch/, cal_write/ (the same counters over the plain
+    device copy of --copy-calibration-mib).  Counters are in KiB per
+    dispatch; each is divided by what it reads per byte the copy moves."""
+    import hashlib
+    f = lambda sub: os.path.join(run_dir, sub, "run_counter_collection.csv")
+    cal_f, cal_w = _counter_means(f("cal_fetch"), "FETCH_SIZE"), _counter_means(f("cal_write"), "WRITE_SIZE")
+    copy_f = [v for n, v in cal_f.items() if "copy" in n.lower()]
+    copy_w = [v for n, v in cal_w.items() if "copy" in n.lower()]
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy kernel in the calibration runs")
+    info = json.load(open(os.path.join(run_dir, "calibration.json")))
+    nbytes = info["copy_calibration_bytes"]
+    ff, fw = copy_f[0] * 1024 / nbytes, copy_w[0] * 1024 / nbytes
+    fetch, write = _counter_means(f("fetch"), "FETCH_SIZE"), _counter_means(f("write"), "WRITE_SIZE")
+    kernels = {}
+    for name, kib in fetch.items():
+        key = next((k for k in TRAFFIC_SOURCES if k in name), None)
+        if key is None or name not in write:
+            continue
+        h = hashlib.sha256()
+        for src in TRAFFIC_SOURCES[key]:
+            h.update(open(os.path.join(ROOT, "exact_tiled_attention_09_amd", "csrc", src), "rb").read())
+        kernels[key] = {"instance": name.split("(")[0].replace("void ", "").replace("miattn::", ""),
+                        "hbm_read_bytes": int(kib * 1024 / ff), "hbm_write_bytes": int(write[name] * 1024 / fw),
+                        "source_sha256": h.hexdigest(), "source_files": TRAFFIC_SOURCES[key]}
+    rec = {"workload": workload, "calibration": {"fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
+                                                 "copy_bytes": nbytes}, "kernels": kernels}
+    out_path = out_path or traffic_record(workload)
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    log_fn(f"wrote {out_path}: {sorted(kernels)}")
+    return rec
+
+
 def kernel_bytes(B, H, Hkv, N, d):
     """Algorithmic HBM bytes of each kernel of a bf16 step: every tensor the
     kernel needs read once and every tensor it produces written once (bf16
@@ -721,7 +781,14 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; its FETCH_SIZE / "
                          "WRITE_SIZE readings calibrate the HBM traffic counters")
+    ap.add_argument("--write-traffic", metavar="RUN_DIR", default=None,
+                    help="no GPU work: write profiles/traffic_<workload>.json from the rocprofv3 counter runs "
+                         "in RUN_DIR (fetch/, write/, cal_fetch/, cal_write/ and calibration.json, the line "
+                         "--copy-calibration-mib printed)")
     args = ap.parse_args(argv)
+    if args.write_traffic:
+        write_traffic_record(args.write_traffic, args.workload, log)
+        return 0
     if args.copy_calibration_mib > 0:
         import torch
         n = args.copy_calibration_mib * (1 << 20) // 4

@@ -468,20 +468,49 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
   }
 
   // dK = scale * acc, dV = acc; accumulator rows are keys, columns features.
+  // In the accumulator layout a lane holds one feature of 16 keys, so direct
+  // stores would be 2 bytes wide; the wave's 32 keys x D of each go through
+  // LDS instead and leave as whole rows, 16 bytes per lane.  Staging: the dK
+  // rows, then the dV rows, row-major with 16-byte chunk c of row r at chunk
+  // c ^ (r mod CH_PER_ROW).  The 8-wave form reuses the wave's own part of
+  // the reduction buffer (read above by this wave alone: its LDS operations
+  // complete in order); the 4-wave form takes a quarter of the arena (every
+  // wave has passed the last barrier after its own LDS reads, and no direct
+  // load is still in flight).
+  uint16_t* st;
+  if constexpr (NW == 8) {
+    static_assert(2 * 32 * D * 2 <= 2 * DB * 16 * 64 * 4, "staging fits the wave's part of the reduction buffer");
+    st = reinterpret_cast<uint16_t*>(reinterpret_cast<float*>(arena) + kblk * 2 * DB * 16 * 64);
+  } else {
+    static_assert(4 * 2 * 32 * D <= 2 * KV_ELEMS + 4 * QT_ELEMS, "staging fits the arena");
+    st = arena + kblk * 2 * 32 * D;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kl = (r >> 2) * 8 + hi * 4 + (r & 3);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = db * 4 + (l32 >> 3);
+      const int so = kl * D + ((c ^ (kl % CH_PER_ROW)) << 3) + (l32 & 7);
+      st[so] = (uint16_t)(pack_bf16x2(dk[db][r] * a.scale, 0.f) & 0xffffu);
+      st[32 * D + so] = (uint16_t)(pack_bf16x2(dv[db][r], 0.f) & 0xffffu);
+    }
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int RPI = 64 / CH_PER_ROW;  // rows per store instruction
   uint16_t* __restrict__ dkp = (uint16_t*)a.dk + sv.kv_base;
   uint16_t* __restrict__ dvp = (uint16_t*)a.dv + sv.kv_base;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = wk0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CH_PER_ROW;
+    const int c = lane % CH_PER_ROW;
+    const int so = r * D + ((c ^ (r % CH_PER_ROW)) << 3);
+    const u32x4 wk = *(const u32x4*)(st + so);
+    const u32x4 wv = *(const u32x4*)(st + 32 * D + so);
+    const int key = wk0 + r;
     if (key < len) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int64_t off = (int64_t)key * sv.kv_stride + db * 32 + l32;
-        const uint32_t kb = pack_bf16x2(dk[db][r] * a.scale, 0.f);
-        const uint32_t vb = pack_bf16x2(dv[db][r], 0.f);
-        dkp[off] = (uint16_t)(kb & 0xffffu);
-        dvp[off] = (uint16_t)(vb & 0xffffu);
-      }
+      *(u32x4*)(dkp + (int64_t)key * sv.kv_stride + c * 8) = wk;
+      *(u32x4*)(dvp + (int64_t)key * sv.kv_stride + c * 8) = wv;
     }
   }
 }
@@ -802,9 +831,15 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     }
   }
 
-  // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers = features).
-  if (row_ok) {
-    uint16_t* __restrict__ dqp = (uint16_t*)a.dq + sv.base + (int64_t)qi * sv.tok_stride;
+  // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers =
+  // features).  As in the forward's epilogue, the wave's 32 x D block goes
+  // through LDS (idle: every wave has passed the last tile's barrier after
+  // waiting for its own LDS reads) so that the global stores are whole rows,
+  // 16 bytes per lane.  Row r is row-major with 16-byte chunk c at c ^ (r mod
+  // CPR); waves 0-5 stage in the K buffers, 6 and 7 in the V buffers.
+  {
+    static_assert(6 * 32 * D <= 3 * TILE && (NW <= 6 || (NW - 6) * 32 * D <= 3 * TILE), "staging fits");
+    uint16_t* stage = wave < 6 ? &sK[0][0] + wave * 32 * D : &sV[0][0] + (wave - 6) * 32 * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -812,8 +847,19 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
         const f32x16& x = dq[db];
         u32x2 w = {pack_bf16x2(x[4 * g + 0] * a.scale, x[4 * g + 1] * a.scale),
                    pack_bf16x2(x[4 * g + 2] * a.scale, x[4 * g + 3] * a.scale)};
-        *(u32x2*)(dqp + db * 32 + g * 8 + hi * 4) = w;
+        const int c = db * 4 + g;
+        *(u32x2*)(stage + l32 * D + ((c ^ (l32 % CPR)) << 3) + hi * 4) = w;
       }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int RPI = 64 / CPR;  // rows per store instruction
+    uint16_t* __restrict__ dqp = (uint16_t*)a.dq + sv.base;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / CPR;
+      const int c = lane % CPR;
+      const u32x4 w = *(const u32x4*)(stage + r * D + ((c ^ (r % CPR)) << 3));
+      if (q_wave0 + r < sv.len) *(u32x4*)(dqp + (int64_t)(q_wave0 + r) * sv.tok_stride + c * 8) = w;
+    }
   }
 }
 

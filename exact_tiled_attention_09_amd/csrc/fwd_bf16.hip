@@ -407,26 +407,42 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   }
 
   // Epilogue: O = O~ / l, LSE = ln 2 * (m + log2 l); a row that saw no
-  // visible key gets O = 0 and LSE = -inf.
+  // visible key gets O = 0 and LSE = -inf.  The wave's 32 x D block of O
+  // goes through LDS (idle after the last barrier: every wave has waited for
+  // its own LDS reads before it) so that the global stores are whole rows,
+  // 16 bytes per lane: in the accumulator layout a store instruction would
+  // touch 32 rows.  Staging rows are row-major with 16-byte chunk c of row r
+  // at chunk c ^ (r mod CPR); waves 0-5 stage in the K buffers, 6 and 7 in
+  // the V buffers.
   uint16_t* __restrict__ op = (uint16_t*)a.o + sv.base;
   const float lt = wave_sum_halves(l);
   const int qi = q_wave0 + l32;
-  if (qi < sv.len) {
-    // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
-    // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
-    const bool dead = (m == kNegInf) && !(lt != lt);
-    const float inv = dead ? 0.f : 1.f / lt;
+  // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
+  // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
+  const bool dead = (m == kNegInf) && !(lt != lt);
+  const float inv = dead ? 0.f : 1.f / lt;
+  static_assert(6 * 32 * D <= 3 * TILE && 2 * 32 * D <= 3 * TILE, "staging fits the tile buffers");
+  uint16_t* stage = wave < 6 ? &sK[0][0] + wave * 32 * D : &sV[0][0] + (wave - 6) * 32 * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& x = o[db];
-        u32x2 w = {pack_bf16x2(x[4 * g + 0] * inv, x[4 * g + 1] * inv),
-                   pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-        *(u32x2*)(op + (int64_t)qi * sv.tok_stride + db * 32 + g * 8 + hi * 4) = w;
-      }
-    if (hi == 0) a.lse[sv.row_base + qi] = dead ? kNegInf : (m + fast_log2(lt)) * kLn2;
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& x = o[db];
+      u32x2 w = {pack_bf16x2(x[4 * g + 0] * inv, x[4 * g + 1] * inv),
+                 pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
+      const int c = db * 4 + g;
+      *(u32x2*)(stage + l32 * D + ((c ^ (l32 % CPR)) << 3) + hi * 4) = w;
+    }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    const int c = lane % CPR;
+    const u32x4 w = *(const u32x4*)(stage + r * D + ((c ^ (r % CPR)) << 3));
+    if (q_wave0 + r < sv.len) *(u32x4*)(op + (int64_t)(q_wave0 + r) * sv.tok_stride + c * 8) = w;
   }
+  if (qi < sv.len && hi == 0) a.lse[sv.row_base + qi] = dead ? kNegInf : (m + fast_log2(lt)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>

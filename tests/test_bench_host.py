@@ -2,6 +2,7 @@
 workloads counts exactly the (query, key) pairs the oracle's mask keeps, and
 the block patterns are valid CSR lists."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -105,3 +106,46 @@ def test_cpu_baseline_cores_are_the_affinity_set():
 def test_new_workloads_are_listed():
     assert "varlen_causal_keypad_h32_d128" in bench.VARLEN_WORKLOADS
     assert "f32_b1_h1_n128_d64" in bench.F32_WORKLOADS
+
+
+def _counter_csv(path, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], r)))
+
+
+def test_traffic_record_from_counter_runs(tmp_path):
+    """The traffic record divides each kernel's mean FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch, rows of one dispatch summed) by what the counters read
+    per byte of the calibration copy, and stamps the kernel sources' hash."""
+    import hashlib
+    import json
+    copy = "__amd_rocclr_copyBuffer"
+    fwd = "void miattn::fwd_stag_kernel<128, true, false, false, 0>(miattn::AttnArgs, int)"
+    nbytes = 1 << 30
+    # the copy reads 0.5 KiB per KiB moved and writes 1.0
+    _counter_csv(str(tmp_path / "cal_fetch" / "run_counter_collection.csv"),
+                 [(1, copy, "FETCH_SIZE", nbytes / 1024 * 0.5)])
+    _counter_csv(str(tmp_path / "cal_write" / "run_counter_collection.csv"),
+                 [(1, copy, "WRITE_SIZE", nbytes / 1024)])
+    (tmp_path / "calibration.json").write_text(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}))
+    # two dispatches, the first split over two rows: mean (300 + 100) KiB read
+    _counter_csv(str(tmp_path / "fetch" / "run_counter_collection.csv"),
+                 [(1, fwd, "FETCH_SIZE", 200.0), (1, fwd, "FETCH_SIZE", 100.0), (2, fwd, "FETCH_SIZE", 100.0)])
+    _counter_csv(str(tmp_path / "write" / "run_counter_collection.csv"),
+                 [(1, fwd, "WRITE_SIZE", 64.0), (2, fwd, "WRITE_SIZE", 64.0)])
+    out = tmp_path / "rec.json"
+    rec = bench.write_traffic_record(str(tmp_path), "w", log_fn=lambda m: None, out_path=str(out))
+    k = rec["kernels"]["fwd_stag_kernel"]
+    assert k["hbm_read_bytes"] == int(200.0 * 1024 / 0.5)
+    assert k["hbm_write_bytes"] == 64 * 1024
+    assert rec["calibration"]["fetch_factor"] == 0.5 and rec["calibration"]["write_factor"] == 1.0
+    h = hashlib.sha256()
+    for src in k["source_files"]:
+        h.update(open(os.path.join(bench.ROOT, "exact_tiled_attention_09_amd", "csrc", src), "rb").read())
+    assert k["source_sha256"] == h.hexdigest()
+    assert json.loads(out.read_text()) == rec
