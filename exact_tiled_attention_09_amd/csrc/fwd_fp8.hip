@@ -397,26 +397,48 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   }
   for (int t = jw_last + 1; t <= ntiles; ++t) end_interval(t);
 
-  // l holds 2^6 times the row sum: O = O~ * s_v / l, LSE = ln 2 * (m + log2 l - 6)
+  // l holds 2^6 times the row sum: O = O~ * s_v / l, LSE = ln 2 * (m + log2 l - 6).
+  // In the accumulator layout a store instruction would touch 32 rows, so
+  // each wave's 32 x 128 block of O goes through LDS (idle: every wave has
+  // passed the last barrier after its own LDS reads) and leaves as row
+  // segments, 16 bytes per lane.  The K and V buffers hold 32 x 64 per wave,
+  // so the block goes in two column halves; a half is row-major with 16-byte
+  // chunk c of row r at chunk c ^ (r mod 8); waves 0-5 stage in the K
+  // buffers, 6 and 7 in the V buffers.
   uint16_t* __restrict__ op = (uint16_t*)a.o + (int64_t)bh * len * D;
   const float lt = wave_sum_halves(l);
   const int qi = q_wave0 + l32;
-  if (qi < len) {
-    // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
-    // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
-    const bool dead = (m == kNegInf) && !(lt != lt);
-    const float inv = dead ? 0.f : a.v_scale[bhk] / lt;
+  // dead: no visible key (max -inf, sum 0); a NaN score leaves the max at
+  // -inf (max ignores NaN) but the sum NaN, and the row comes out NaN
+  const bool dead = (m == kNegInf) && !(lt != lt);
+  const float inv = dead ? 0.f : a.v_scale[bhk] / lt;
+  constexpr int HW = D / 2;  // columns per half
+  static_assert(6 * 32 * HW * 2 <= 3 * KTILE && 2 * 32 * HW * 2 <= 3 * VTILE, "staging fits the tile buffers");
+  uint16_t* stage = wave < 6 ? reinterpret_cast<uint16_t*>(&sK[0][0]) + wave * 32 * HW
+                             : reinterpret_cast<uint16_t*>(&sV[0][0]) + (wave - 6) * 32 * HW;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int db = 2 * half; db < 2 * half + 2; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& x = o[db];
         u32x2 wv = {pack_bf16x2(x[4 * g + 0] * inv, x[4 * g + 1] * inv),
                     pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-        *(u32x2*)(op + (int64_t)qi * D + db * 32 + g * 8 + hi * 4) = wv;
+        const int c = (db - 2 * half) * 4 + g;
+        *(u32x2*)(stage + l32 * HW + ((c ^ (l32 % 8)) << 3) + hi * 4) = wv;
       }
-    if (hi == 0) a.lse[(int64_t)bh * len + qi] = dead ? kNegInf : (m + fast_log2(lt) - kPScaleLog2) * kLn2;
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * 8 + lane / 8;
+      const int c = lane % 8;
+      const u32x4 w = *(const u32x4*)(stage + r * HW + ((c ^ (r % 8)) << 3));
+      if (q_wave0 + r < len) *(u32x4*)(op + (int64_t)(q_wave0 + r) * D + half * HW + c * 8) = w;
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads are done before the next half's writes
   }
+  if (qi < len && hi == 0) a.lse[(int64_t)bh * len + qi] = dead ? kNegInf : (m + fast_log2(lt) - kPScaleLog2) * kLn2;
 }
 
 // ------------------------------------------------------------------ launchers
