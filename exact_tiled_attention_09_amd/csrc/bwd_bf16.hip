@@ -15,11 +15,12 @@
 //     P = exp(S - LSE), forms dP = dO V^T and dS, and accumulates dV += P^T dO
 //     and dK += dS^T Q.  S and dS leave the accumulator already in A-operand
 //     layout (lane = key); dO and Q enter through the LDS transpose read.
-//  3. bwd_dq: query-tile outer loop, shaped like the forward: one workgroup
-//     per (sequence, head, 256-row query tile), 8 waves of 32 rows with Q and
-//     dO resident in registers.  For every key tile up to the diagonal it
-//     rebuilds S^T = K Q^T and dP^T = V dO^T (lane = query, so LSE and D are
-//     per-lane scalars) and accumulates dQ^T += K^T dS^T.
+//  3. bwd_dq: query-tile outer loop, shaped like the forward (and on its
+//     staggered schedule): one workgroup per (sequence, head, 256-row query
+//     tile), 8 waves of 32 rows with Q and dO resident in registers.  For
+//     every key tile up to the diagonal it rebuilds S^T = K Q^T and
+//     dP^T = V dO^T (lane = query, so LSE and D are per-lane scalars) and
+//     accumulates dQ^T += K^T dS^T.
 // The pages accumulate dQ with atomic adds from the key-tile loop.  Here dQ
 // gets its own pass instead: it re-forms S and dP (two more N^2 d products),
 // but on MI355X device-scope float atomics are performed past the per-XCD L2,
@@ -516,13 +517,23 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
 }
 
 // ---------------------------------------------------------------- kernel 3
-// K and V tiles of 64 keys travel from global memory straight into LDS
-// (three buffers each, fetched two tiles ahead, as in the forward's
-// direct-load form); before the barrier that ends tile j each wave waits only
-// for its own loads of tile j+1.  Rows past the sequence repeat its last row
-// and are masked.
+// The forward's staggered schedule: one barrier per 64-key tile, and waves w
+// and w + 4 on one SIMD half a tile apart.  Every wave runs, for key tile j,
+//   S^T_j = K_j Q^T and dP^T_j = V_j dO^T (MFMA),  dS_j (VALU),
+//   dQ^T += K_j^T dS^T_j (MFMA),
+// and interval j ends after S/dP_j for the late waves (4-7) and after dS_j for
+// the early ones: within an interval an early wave issues dQ_{j-1}, S/dP_j and
+// then dS_j, while its partner computes dS_{j-1} and then dQ_{j-1}, S/dP_j,
+// so one wave's vector work overlaps the other's matrix work.  K and V tiles
+// travel from global memory straight into LDS, four slots each, tile t + 2
+// fetched at the start of interval t: K_j is read in interval j (S_j) and
+// again in interval j + 1 (dQ_j), so its slot is refilled only in interval
+// j + 2.  Before the barrier that ends interval t each wave waits only for its
+// own loads of tile t + 1.  Rows past the sequence repeat its last row and
+// are masked.
 template <int D, int NW, bool CAUSAL, bool VARLEN, bool KPAD, int MASK = kMaskPlain>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qtiles) {
+  static_assert(NW == 8, "two waves per SIMD");
   constexpr int BC = 64;                 // keys per tile
   constexpr int BR = NW * 32;            // query rows per workgroup
   constexpr int KS = D / 16;
@@ -531,12 +542,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;
   constexpr int LPT = BC * CPR / NT;     // direct loads per thread per tensor and tile
+  constexpr int NS = 4;                  // tile slots per tensor
   static_assert(LPT * NT == BC * CPR, "tile chunks must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
-  __shared__ uint8_t s_valid[3][BC];
-  __shared__ uint32_t s_anypad[3];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NS][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NS][TILE];
+  __shared__ uint8_t s_valid[NS][BC];
+  __shared__ uint32_t s_anypad[NS];
 
   int bh, tile;
   // causal masks, windows and block lists: groups of four heads per XCD,
@@ -558,6 +570,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const bool late = wave >= 4;  // the partner of wave w on its SIMD is w + 4
   const int q_wave0 = q_tile0 + wave * 32;
   const int qi = q_wave0 + l32;  // this lane's query row (columns of S^T)
   const float c = a.scale_log2;
@@ -583,6 +596,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   if constexpr (MASK == kMaskPlain) {
     const int kv_end = CAUSAL ? min(kv_len, q_tile0 + BR) : kv_len;
     ntiles = (kv_end + BC - 1) / BC;
+    jw_last = CAUSAL ? min(ntiles - 1, (q_wave0 + 31) / BC) : ntiles - 1;
   } else if constexpr (MASK == kMaskWindow) {
     jt0 = max(0, q_tile0 - a.win_left) / BC;
     const int kv_end = min(kv_len, q_tile0 + BR + a.win_right);
@@ -592,6 +606,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   } else {
     static_assert(BR == 2 * kSparseBlock, "two query blocks per workgroup");
     ntiles = 2 * build_key_block_list<NT, CAUSAL>(a, q_tile0, s_bflag, s_blist, &s_bcount);
+    jw_last = ntiles - 1;
   }
   auto tile_of = [&](int r) __attribute__((always_inline)) -> int {
     if constexpr (MASK == kMaskPlain) return r;
@@ -606,7 +621,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
       const int kt0 = ((e & 0xfff) * 2 + (r & 1)) * BC;
       return ((e >> (12 + (wave >> 2))) & 1) != 0 && kt0 < kv_len && (!CAUSAL || kt0 <= q_wave0 + 31);
     } else {
-      return !CAUSAL || r * BC <= q_wave0 + 31;
+      return true;
     }
   };
 
@@ -618,24 +633,21 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     src_row[i] = row;
     src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
-  // Load number n (0 .. 2*LPT-1) of this thread for tile j: K for even n, V
-  // for odd n, chunk n / 2.
-  auto issue_part = [&](int j, int n) {
-    const int i = n >> 1;
-    const int key = min(tile_of(j) * BC + src_row[i], kv_len - 1);
-    const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
-    if (n & 1) lds_dma16(vp + off, sV[j % 3] + (i * NT + wave * 64) * 8);
-    else lds_dma16(kp + off, sK[j % 3] + (i * NT + wave * 64) * 8);
-  };
-  auto issue = [&](int j) {
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int k0 = tile_of(j) * BC;
 #pragma unroll
-    for (int n = 0; n < 2 * LPT; ++n) issue_part(j, n);
+    for (int i = 0; i < LPT; ++i) {
+      const int key = min(k0 + src_row[i], kv_len - 1);
+      const int64_t off = (int64_t)key * sv.kv_stride + src_col[i];
+      lds_dma16(kp + off, sK[j % NS] + (i * NT + wave * 64) * 8);
+      lds_dma16(vp + off, sV[j % NS] + (i * NT + wave * 64) * 8);
+    }
   };
   // Key-validity flags of a tile, by wave 0: the raw byte is loaded early
   // and converted only when stored, so the wave does not wait in between.
   uint32_t rvalid = 1u;
   int rkey = 0;
-  auto load_flags = [&](int j) {
+  auto load_flags = [&](int j) __attribute__((always_inline)) {
     if constexpr (KPAD) {
       if (wave == 0) {
         rkey = j * BC + lane;
@@ -643,13 +655,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
       }
     }
   };
-  auto store_flags = [&](int j) {
+  auto store_flags = [&](int j) __attribute__((always_inline)) {
     if constexpr (KPAD) {
       if (wave == 0) {
         const uint32_t ok = (rkey >= kv_len || rvalid != 0u) ? 1u : 0u;  // keys past the end are masked anyway
-        s_valid[j % 3][lane] = (uint8_t)ok;
+        s_valid[j % NS][lane] = (uint8_t)ok;
         const bool any = wave_any(ok == 0u);
-        if (lane == 0) s_anypad[j % 3] = any ? 1u : 0u;
+        if (lane == 0) s_anypad[j % NS] = any ? 1u : 0u;
       }
     }
   };
@@ -665,9 +677,145 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
 #pragma unroll
     for (int db = 0; db < DB; ++db) troff[R][db] = swz_off<D>(8 * R + tr_r, db * 32 + tr_c);
 
+  float lse2 = 0.f, dd = 0.f;
+  f32x16 s[2], dp[2];  // S^T and dP^T of the tile formed last (then dS^T in dp)
+  bf16x8 dsb[4];       // packed dS^T of the tile whose vector part ran last
+
+  // Whether block kb (32 keys) of the tile starting at key kt0 lies wholly
+  // above the diagonal for this wave's rows (then its products are skipped
+  // and its dS is zero).
+  auto above = [&](int kt0, int kb) __attribute__((always_inline)) -> bool {
+    return CAUSAL && kt0 + kb * 32 > q_wave0 + 31;
+  };
+  // S^T and dP^T of a tile from slot SL, both 32-key blocks, K and V operands
+  // read one k-step ahead across the two blocks (a deeper ring measured no
+  // faster and holds eight more registers).
+  auto mma_sdp = [&](auto slot_c, int kt0) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint16_t* sk = sK[SL];
+    const uint16_t* svv = sV[SL];
+    const bool skip1 = above(kt0, 1);
+    constexpr int NI = 2 * KS;
+    bf16x8 opk[2], opv[2];
+    auto sread = [&](int i, int u) __attribute__((always_inline)) {
+      const int kb = i / KS;
+      const int ks = i % KS;
+      opk[u] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
+      opv[u] = as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks]));
+    };
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+    sread(0, 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int kb = i / KS;
+      const int ks = i % KS;
+      if (kb == 1 && skip1) break;
+      if (i + 1 < NI) sread(i + 1, (i + 1) % 2);
+      s[kb] = mfma_bf16(opk[i % 2], qf[ks], s[kb]);
+      dp[kb] = mfma_bf16(opv[i % 2], gf[ks], dp[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // dS^T = P^T o (dP^T - D) with P^T = exp2(S^T c - LSE log2 e), packed to
+  // bf16 for the dQ products; masked entries get P = 0.
+  auto vpart = [&](int j) __attribute__((always_inline)) {
+    const int kt0 = tile_of(j) * BC;
+    const int slot = j % NS;
+    bool need_mask = kt0 + BC > kv_len;
+    if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
+    if (KPAD) need_mask = need_mask || (s_anypad[slot] != 0u);
+    if (MASK == kMaskWindow)
+      need_mask = need_mask || (kt0 < q_wave0 + 31 - a.win_left) || (kt0 + BC - 1 > q_wave0 + a.win_right);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (above(kt0, kb)) {
+        dsb[kb * 2] = bf16x8{};
+        dsb[kb * 2 + 1] = bf16x8{};
+        continue;
+      }
+      float cc = c;
+      if (need_mask) {
+        // Masked entries get an exponent argument of -inf (exp2 -> 0), with
+        // the scale applied before the select (see the key-tile pass).
+        cc = 1.f;
+        const int q_m = pin_in_branch(qi);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          const int key = kt0 + kl;
+          bool vis = key < kv_len;
+          if (CAUSAL) vis = vis && key <= q_m;
+          if (KPAD) vis = vis && s_valid[slot][kl] != 0;
+          if (MASK == kMaskWindow) vis = vis && key >= q_m - a.win_left && key <= q_m + a.win_right;
+          s[kb][r] = vis ? s[kb][r] * c : kNegInf;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], cc, -lse2));
+        dp[kb][r] = p * (dp[kb][r] - dd);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        dsb[kb * 2 + t] = pack_bf16x8(dp[kb][8 * t + 0], dp[kb][8 * t + 1], dp[kb][8 * t + 2], dp[kb][8 * t + 3],
+                                      dp[kb][8 * t + 4], dp[kb][8 * t + 5], dp[kb][8 * t + 6], dp[kb][8 * t + 7]);
+    }
+  };
+  // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read, three
+  // MFMAs ahead across the two blocks.
+  auto mma_dq = [&](auto slot_c, int kt0) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint16_t* sk = sK[SL];
+    constexpr int NKK = 2 * DB;
+    constexpr int NI = 2 * NKK;
+    constexpr int PF = 3;
+    const bool skip1 = above(kt0, 1);
+    auto tread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      const int kb = i / NKK;
+      const int ii = i % NKK;
+      const uint16_t* kt = sk + (kb * 32 + 16 * (ii / DB)) * D;
+      return join_u32x2(lds_read_tr16(kt + troff[0][ii % DB]), lds_read_tr16(kt + troff[1][ii % DB]));
+    };
+    bf16x8 ka[NI];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ka[i] = tread(i);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int kb = i / NKK;
+      const int ii = i % NKK;
+      if (kb == 1 && skip1) break;
+      if (i + PF < NI) ka[i + PF] = tread(i + PF);
+      dq[ii % DB] = mfma_bf16(ka[i], dsb[kb * 2 + ii / DB], dq[ii % DB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Start of interval t: fetch tile t + 2 (and its flags, stored at the end
+  // of the interval).  End of interval t: tile t + 1 must have landed (the
+  // interval's own loads may still be in flight), barrier, then start t + 1.
+  auto begin_interval = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 < ntiles) {
+      load_flags(t + 2);
+      issue(t + 2);
+    }
+  };
+  auto end_interval = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 < ntiles) {
+      store_flags(t + 2);
+      barrier_vmem_n<2 * LPT>();
+    } else {
+      barrier_vmem_n<0>();
+    }
+    begin_interval(t + 1);
+  };
+
   // An empty block list leaves dQ = 0.
   if (MASK != kMaskBlocks || ntiles > 0) {
-    // Prologue: start tiles 0 and 1, then load this wave's Q, dO, LSE and D
+    // Prologue: tiles 0 and 1 in flight, then this wave's Q, dO, LSE and D
     // rows; one wait (which the compiler sees, so the loop waits for none of
     // these loads again) covers all of them.
     load_flags(0);
@@ -692,8 +840,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     }
     // a dead or out-of-range row gets P = 0
     const float lse_raw = a.lse[sv.row_base + qc];
-    const float lse2 = (!row_ok || lse_raw == kNegInf) ? kPosInf : lse_raw * kLog2e;
-    float dd;
+    lse2 = (!row_ok || lse_raw == kNegInf) ? kPosInf : lse_raw * kLog2e;
     if (a.dq_writes_d) {
       // D = rowsum(dO o O) in the summation order of the D pre-pass, so both
       // give the same bits: each 8-feature chunk in order (this lane holds
@@ -727,118 +874,43 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     barrier_vmem_n<0>();
+    begin_interval(0);
 
-    // One key tile from buffer slot BUF (= j % 3, a compile-time constant).
-    auto step = [&](int j, auto buf_c) {
-      constexpr int buf = decltype(buf_c)::value;
-      const bool fetch = j + 2 < ntiles;
-      const int kt0 = tile_of(j) * BC;
-      const bool live = wave_live(j);
-      if (fetch) load_flags(j + 2);
-      // A wave with work spreads its loads of tile j+2 over the first block's
-      // S^T / dP^T MFMAs; an idle wave issues them at once.
-      if (fetch && !live) issue(j + 2);
-      if (live) {
-        const uint16_t* sk = sK[buf];
-        const uint16_t* svv = sV[buf];
-        bool need_mask = kt0 + BC > kv_len;
-        if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
-        if (KPAD) need_mask = need_mask || (s_anypad[buf] != 0u);
-        if (MASK == kMaskWindow)
-          need_mask = need_mask || (kt0 < q_wave0 + 31 - a.win_left) || (kt0 + BC - 1 > q_wave0 + a.win_right);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (CAUSAL && kt0 + kb * 32 > q_wave0 + 31) continue;  // block wholly above the diagonal
-          // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query column).
-          // K and V operands read two k-steps ahead of their MFMAs.
-          f32x16 s = f32x16{}, dp = f32x16{};
-          bf16x8 opk[3], opv[3];
-          auto sread = [&](int ks, int u) __attribute__((always_inline)) {
-            opk[u] = as_bf16x8(*(const u32x4*)(sk + kb * 32 * D + koff[ks]));
-            opv[u] = as_bf16x8(*(const u32x4*)(svv + kb * 32 * D + koff[ks]));
-          };
-          sread(0, 0);
-          sread(1, 1);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS) sread(ks + 2, (ks + 2) % 3);
-            s = mfma_bf16(opk[ks % 3], qf[ks], s);
-            dp = mfma_bf16(opv[ks % 3], gf[ks], dp);
-            if (kb == 0 && fetch) {  // block 0 is never skipped when the wave is live
-#pragma unroll
-              for (int n = ks * 2 * LPT / KS; n < (ks + 1) * 2 * LPT / KS; ++n) issue_part(j + 2, n);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          float cc = c;
-          if (need_mask) {
-            // Masked entries get an exponent argument of -inf (exp2 -> 0),
-            // with the scale applied before the select (see the key-tile pass).
-            cc = 1.f;
-            const int q_m = pin_in_branch(qi);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kl = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-              const int key = kt0 + kl;
-              bool vis = key < kv_len;
-              if (CAUSAL) vis = vis && key <= q_m;
-              if (KPAD) vis = vis && s_valid[buf][kl] != 0;
-              if (MASK == kMaskWindow) vis = vis && key >= q_m - a.win_left && key <= q_m + a.win_right;
-              s[r] = vis ? s[r] * c : kNegInf;
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(__builtin_fmaf(s[r], cc, -lse2));
-            dp[r] = p * (dp[r] - dd);
-          }
-          // dQ^T += K^T dS^T, 16 keys per MFMA: K through the transpose read,
-          // three MFMAs ahead.
-          bf16x8 dsb[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            dsb[t] = pack_bf16x8(dp[8 * t + 0], dp[8 * t + 1], dp[8 * t + 2], dp[8 * t + 3],
-                                 dp[8 * t + 4], dp[8 * t + 5], dp[8 * t + 6], dp[8 * t + 7]);
-          constexpr int NKK = 2 * DB;
-          constexpr int PF = 3;
-          auto tread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-            const uint16_t* kt = sk + (kb * 32 + 16 * (i / DB)) * D;
-            return join_u32x2(lds_read_tr16(kt + troff[0][i % DB]), lds_read_tr16(kt + troff[1][i % DB]));
-          };
-          bf16x8 ka[NKK];
-#pragma unroll
-          for (int i = 0; i < PF; ++i) ka[i] = tread(i);
-#pragma unroll
-          for (int i = 0; i < NKK; ++i) {
-            if (i + PF < NKK) ka[i + PF] = tread(i + PF);
-            dq[i % DB] = mfma_bf16(ka[i], dsb[i / DB], dq[i % DB]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+    // Every wave passes ntiles + 1 barriers after the prologue: one per key
+    // tile it works on or skips, then the remaining intervals up to ntiles.
+    auto body = [&](int j, auto slot_c) __attribute__((always_inline)) {
+      if constexpr (MASK != kMaskPlain) {
+        if (!wave_live(j)) {
+          end_interval(j);
+          return;
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-
-      if (fetch) store_flags(j + 2);
-      // this wave's loads of tile j + 1 have landed (those of j + 2 may not)
-      if (fetch) barrier_vmem_n<2 * LPT>();
-      else barrier_vmem_n<0>();
+      const int kt0 = tile_of(j) * BC;
+      mma_sdp(slot_c, kt0);
+      if (late) end_interval(j);
+      vpart(j);
+      if (!late) end_interval(j);
+      mma_dq(slot_c, kt0);
     };
-    for (int j = 0; j < ntiles; j += 3) {
-      step(j, std::integral_constant<int, 0>{});
-      if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
-      if (j + 2 < ntiles) step(j + 2, std::integral_constant<int, 2>{});
+    const int j_end = MASK == kMaskPlain ? jw_last : ntiles - 1;
+    for (int j = 0; j <= j_end; j += NS) {
+      body(j, std::integral_constant<int, 0>{});
+      if (j + 1 <= j_end) body(j + 1, std::integral_constant<int, 1>{});
+      if (j + 2 <= j_end) body(j + 2, std::integral_constant<int, 2>{});
+      if (j + 3 <= j_end) body(j + 3, std::integral_constant<int, 3>{});
     }
+    for (int t = j_end + 1; t <= ntiles; ++t) end_interval(t);
   }
 
   // dQ = scale * acc; the accumulator holds dQ^T (lane = query, registers =
   // features).  As in the forward's epilogue, the wave's 32 x D block goes
-  // through LDS (idle: every wave has passed the last tile's barrier after
-  // waiting for its own LDS reads) so that the global stores are whole rows,
-  // 16 bytes per lane.  Row r is row-major with 16-byte chunk c at c ^ (r mod
-  // CPR); waves 0-5 stage in the K buffers, 6 and 7 in the V buffers.
+  // through LDS (idle: every wave has passed the last barrier after waiting
+  // for its own LDS reads and loads) so that the global stores are whole
+  // rows, 16 bytes per lane.  Row r is row-major with 16-byte chunk c at
+  // c ^ (r mod CPR); waves 0-5 stage in the K buffers, 6 and 7 in the V
+  // buffers.
   {
-    static_assert(6 * 32 * D <= 3 * TILE && (NW <= 6 || (NW - 6) * 32 * D <= 3 * TILE), "staging fits");
+    static_assert(6 * 32 * D <= NS * TILE && (NW - 6) * 32 * D <= NS * TILE, "staging fits");
     uint16_t* stage = wave < 6 ? &sK[0][0] + wave * 32 * D : &sV[0][0] + (wave - 6) * 32 * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -847,8 +919,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
         const f32x16& x = dq[db];
         u32x2 w = {pack_bf16x2(x[4 * g + 0] * a.scale, x[4 * g + 1] * a.scale),
                    pack_bf16x2(x[4 * g + 2] * a.scale, x[4 * g + 3] * a.scale)};
-        const int c = db * 4 + g;
-        *(u32x2*)(stage + l32 * D + ((c ^ (l32 % CPR)) << 3) + hi * 4) = w;
+        const int cc = db * 4 + g;
+        *(u32x2*)(stage + l32 * D + ((cc ^ (l32 % CPR)) << 3) + hi * 4) = w;
       }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     constexpr int RPI = 64 / CPR;  // rows per store instruction
@@ -856,9 +928,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = i * RPI + lane / CPR;
-      const int c = lane % CPR;
-      const u32x4 w = *(const u32x4*)(stage + r * D + ((c ^ (r % CPR)) << 3));
-      if (q_wave0 + r < sv.len) *(u32x4*)(dqp + (int64_t)(q_wave0 + r) * sv.tok_stride + c * 8) = w;
+      const int cc = lane % CPR;
+      const u32x4 w = *(const u32x4*)(stage + r * D + ((cc ^ (r % CPR)) << 3));
+      if (q_wave0 + r < sv.len) *(u32x4*)(dqp + (int64_t)(q_wave0 + r) * sv.tok_stride + cc * 8) = w;
     }
   }
 }
