@@ -63,8 +63,17 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   constexpr int TILE = BC * D;
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;
-  constexpr int LPT = BC * CPR / NT;  // direct loads per thread per tensor and tile
-  static_assert(LPT * NT == BC * CPR, "tile chunks must divide evenly");
+  // Who issues the K/V tile loads.  d = 128: every wave, right after the
+  // barrier that opens an interval.  d = 64: only the early waves, spread
+  // over their MFMA phases (one load per four MFMAs): at d = 64 the matrix
+  // phases are half as long as the softmax, so the early waves' matrix phase
+  // has room for them, while loads issued after the barrier delay the
+  // late waves' softmax, the longer phase (measured 5-9% faster at d = 64;
+  // 2-3% slower at d = 128, where the two phases are balanced).
+  constexpr bool SPREAD = D == 64;
+  constexpr int NLD = SPREAD ? NT / 2 : NT;  // threads that issue tile loads
+  constexpr int LPT = BC * CPR / NLD;        // direct loads per such thread per tensor and tile
+  static_assert(LPT * NLD == BC * CPR, "tile chunks must divide evenly");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
@@ -162,24 +171,35 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     }
   };
 
-  // Direct-load sources: LDS chunk p = i*NT + tid of a tile holds row p / CPR,
-  // logical chunk (p % CPR) ^ swz(row).  Rows past the sequence repeat its
-  // last row (finite values, masked in the softmax).
+  // Direct-load sources: LDS chunk p = i*NLD + t of a tile (t the issuing
+  // thread) holds row p / CPR, logical chunk (p % CPR) ^ swz(row).  Rows past
+  // the sequence repeat its last row (finite values, masked in the softmax).
   int src_row[LPT], src_col[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int pch = i * NT + tid;
+    const int pch = i * NLD + (SPREAD ? (tid & (NLD - 1)) : tid);
     const int row = pch / CPR;
     src_row[i] = row;
     src_col[i] = ((pch % CPR) ^ swz<D>(row)) << 3;
   }
+  // Load i of the key tile starting at key k0 into dst.  In the spread form
+  // the wave's LDS base passes through an empty asm at each call, so the
+  // compiler forms every M0 value where it is used rather than keeping one
+  // scalar register per slot and chunk.
+  auto dma = [&](const uint16_t* src, uint16_t* dst, int k0, int i) __attribute__((always_inline)) {
+    const int key = min(k0 + src_row[i], kv_len - 1);
+    if constexpr (SPREAD) {
+      uint32_t wb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MIATTN_LDS void*)(dst + wave * 64 * 8));
+      __asm__ volatile("" : "+s"(wb));
+      lds_dma16_m0(src + (int64_t)key * sv.kv_stride + src_col[i], wb + i * NLD * 16);
+    } else {
+      lds_dma16(src + (int64_t)key * sv.kv_stride + src_col[i], dst + (i * NLD + wave * 64) * 8);
+    }
+  };
   auto issue = [&](const uint16_t* src, uint16_t* dst, int j) __attribute__((always_inline)) {
     const int k0 = tile_of(j) * BC;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int key = min(k0 + src_row[i], kv_len - 1);
-      lds_dma16(src + (int64_t)key * sv.kv_stride + src_col[i], dst + (i * NT + wave * 64) * 8);
-    }
+    for (int i = 0; i < LPT; ++i) dma(src, dst, k0, i);
   };
   uint32_t rvalid = 1u;
   auto load_flags = [&](int j) __attribute__((always_inline)) {
@@ -219,8 +239,17 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   // The MFMA phases read their LDS operands ahead of use (K two k-steps,
   // V three MFMAs), so that a wave whose partner is busy with vector work
   // does not wait a full LDS latency before every MFMA.
-  auto mma_s = [&](auto slot_c) __attribute__((always_inline)) {
-    const uint16_t* kt = sK[decltype(slot_c)::value];
+  // Spread form: S_j carries the early wave's loads of V_{j+1}, P_j V_j those
+  // of K_{j+3} (with the key flags of tile j+3).
+  constexpr int S_STEP = KS / LPT;       // k-steps of S between two loads
+  constexpr int PV_STEP = 4 * DB / LPT;  // MFMAs of P V between two loads
+  static_assert(!SPREAD || (S_STEP * LPT == KS && PV_STEP * LPT == 4 * DB && S_STEP >= 1 && PV_STEP >= 1),
+                "load spread");
+  auto mma_s = [&](auto slot_c, int j) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint16_t* kt = sK[SL];
+    const bool ld = SPREAD && !late && j + 1 < ntiles;
+    const int k0n = ld ? tile_of(j + 1) * BC : 0;
     s[0] = f32x16{};
     s[1] = f32x16{};
     bf16x8 ka[3][2];
@@ -235,13 +264,18 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
       if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(ka[ks % 3][kb], qf[ks], s[kb]);
+      if (SPREAD && ks % S_STEP == S_STEP - 1 && ld) dma(vp, sV[(SL + 1) % 3], k0n, ks / S_STEP);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto mma_pv = [&](auto slot_c) __attribute__((always_inline)) {
+  auto mma_pv = [&](auto slot_c, int j) __attribute__((always_inline)) {
     constexpr int NPV = 4 * DB;
     constexpr int PF = 3;
-    const uint16_t* vt = sV[decltype(slot_c)::value];
+    constexpr int SL = decltype(slot_c)::value;
+    const uint16_t* vt = sV[SL];
+    const bool ld = SPREAD && !late && j + 3 < ntiles;
+    const int k0n = ld ? tile_of(j + 3) * BC : 0;
+    if (ld) load_flags(j + 3);
     auto vread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
       const uint16_t* v0 = vt + (i / DB) * 16 * D;  // keys 16 (i / DB) .. +15
       return join_u32x2(lds_read_tr16(v0 + voff[0][i % DB]), lds_read_tr16(v0 + voff[1][i % DB]));
@@ -253,6 +287,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     for (int i = 0; i < NPV; ++i) {
       if (i + PF < NPV) va[i + PF] = vread(i + PF);
       o[i % DB] = mfma_bf16(va[i], p[i / DB], o[i % DB]);
+      if (SPREAD && i % PV_STEP == PV_STEP - 1 && ld) dma(kp, sK[SL], k0n, i / PV_STEP);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -346,8 +381,12 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     l += rs;
   };
 
-  // Start of interval t: fetch K_{t+2} and V_{t+1} (and the flags of tile
-  // t+2, stored at the end of the interval).
+  // Interval t fetches K_{t+2} (with the flags of tile t+2, stored at the end
+  // of the interval) and V_{t+1}: every wave right after the barrier that
+  // opens the interval, or, in the spread form, an early wave inside
+  // P_{t-1} V_{t-1} and S_t (right after the barrier when it skips one of
+  // them).  The barrier ending interval t needs K_{t+1} and V_t (interval
+  // t-1's loads) and lets interval t's own loads stay in flight.
   auto begin_interval = [&](int t) __attribute__((always_inline)) {
     if (t + 2 < ntiles) {
       load_flags(t + 2);
@@ -355,32 +394,80 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     }
     if (t + 1 < ntiles) issue(vp, sV[(t + 1) % 3], t + 1);
   };
-  // End of interval t: K_{t+1} and V_t must have landed (the loads of the
-  // interval itself may still be in flight), barrier, then start t+1.
+  // Whether this wave computes key tile j (S_j, softmax_j and P_j V_j).
+  auto live = [&](int j) __attribute__((always_inline)) -> bool {
+    if (j < 0 || j >= ntiles) return false;
+    if constexpr (MASK == kMaskPlain) return j <= jw_last;
+    else return wave_live(j);
+  };
   auto end_interval = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) store_flags(t + 2);
-    const int pending = (t + 2 < ntiles ? LPT : 0) + (t + 1 < ntiles ? LPT : 0);
-    if (pending == 2 * LPT) barrier_vmem_n<2 * LPT>();
-    else if (pending == LPT) barrier_vmem_n<LPT>();
-    else barrier_vmem_n<0>();
-    begin_interval(t + 1);
+    if constexpr (SPREAD) {
+      if (!late) {
+        if (t + 2 < ntiles) store_flags(t + 2);
+        const int pending = (t + 2 < ntiles ? LPT : 0) + (t + 1 < ntiles ? LPT : 0);
+        if (pending == 2 * LPT) barrier_vmem_n<2 * LPT>();
+        else if (pending == LPT) barrier_vmem_n<LPT>();
+        else barrier_vmem_n<0>();
+        if (!live(t) && t + 3 < ntiles) {
+          load_flags(t + 3);
+          issue(kp, sK[(t + 3) % 3], t + 3);
+        }
+        if (!live(t + 1) && t + 2 < ntiles) issue(vp, sV[(t + 2) % 3], t + 2);
+      } else {
+        barrier_vmem_n<0>();  // the late waves hold no loads
+      }
+    } else {
+      if (t + 2 < ntiles) store_flags(t + 2);
+      const int pending = (t + 2 < ntiles ? LPT : 0) + (t + 1 < ntiles ? LPT : 0);
+      if (pending == 2 * LPT) barrier_vmem_n<2 * LPT>();
+      else if (pending == LPT) barrier_vmem_n<LPT>();
+      else barrier_vmem_n<0>();
+      begin_interval(t + 1);
+    }
   };
 
   // An empty block list leaves every row without a key (O = 0, LSE = -inf).
   if (MASK != kMaskBlocks || ntiles > 0) {
-    // Prologue: K_0, K_1, V_0 and the flags of tiles 0 and 1.
-    load_flags(0);
-    store_flags(0);
-    issue(kp, sK[0], 0);
-    if (ntiles > 1) {
-      load_flags(1);
-      store_flags(1);
-      issue(kp, sK[1], 1);
+    // Prologue: K_0, K_1, V_0 and the flags of tiles 0 and 1; in the spread
+    // form (early waves only) also interval 0's K_2, since no P V precedes
+    // S_0.  K_0 must land.
+    if constexpr (SPREAD) {
+      if (!late) {
+        load_flags(0);
+        store_flags(0);
+        issue(kp, sK[0], 0);
+        if (ntiles > 1) {
+          load_flags(1);
+          store_flags(1);
+          issue(kp, sK[1], 1);
+        }
+        issue(vp, sV[0], 0);
+        if (ntiles > 2) {
+          load_flags(2);
+          issue(kp, sK[2], 2);
+        }
+        const int pending = (ntiles > 1 ? LPT : 0) + LPT + (ntiles > 2 ? LPT : 0);
+        if (pending == 3 * LPT) barrier_vmem_n<3 * LPT>();
+        else if (pending == 2 * LPT) barrier_vmem_n<2 * LPT>();
+        else barrier_vmem_n<LPT>();
+        if (!live(0) && ntiles > 1) issue(vp, sV[1], 1);
+      } else {
+        barrier_vmem_n<0>();
+      }
+    } else {
+      load_flags(0);
+      store_flags(0);
+      issue(kp, sK[0], 0);
+      if (ntiles > 1) {
+        load_flags(1);
+        store_flags(1);
+        issue(kp, sK[1], 1);
+      }
+      issue(vp, sV[0], 0);
+      if (ntiles > 1) barrier_vmem_n<2 * LPT>();  // K_0 has landed
+      else barrier_vmem_n<LPT>();
+      begin_interval(0);
     }
-    issue(vp, sV[0], 0);
-    if (ntiles > 1) barrier_vmem_n<2 * LPT>();  // K_0 has landed
-    else barrier_vmem_n<LPT>();
-    begin_interval(0);
 
     // Every wave passes ntiles + 1 barriers after the prologue: one per key
     // tile it works on or skips, then the remaining intervals up to ntiles.
@@ -391,11 +478,11 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
           return;
         }
       }
-      mma_s(slot_c);
+      mma_s(slot_c, j);
       if (late) end_interval(j);
       softmax(j);
       if (!late) end_interval(j);
-      mma_pv(slot_c);
+      mma_pv(slot_c, j);
     };
     const int j_end = MASK == kMaskPlain ? jw_last : ntiles - 1;
     for (int j = 0; j <= j_end; j += 3) {

@@ -364,6 +364,12 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m));
 }
 
+// The same load with the M0 value (the wave's LDS destination in bytes,
+// wave-uniform) given directly, for callers that form it themselves.
+__device__ __forceinline__ void lds_dma16_m0(const void* g, uint32_t m0_value) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0_value));
+}
+
 // Workgroup barrier for kernels that keep direct-to-LDS loads in flight
 // across it.  __syncthreads() fences LDS, which makes the compiler wait for
 // every outstanding direct load (vmcnt(0)) first; here the wave waits until
