@@ -258,16 +258,40 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   // Direct loads: one 16-byte chunk per thread per tile and tensor.  K tile
   // rows are 128 bytes (8 chunks, chunk c of row r stored at c ^ (r/2 % 8));
   // V^T tile rows are 64 bytes (4 chunks, at c ^ (r/4 % 4)).
-  const int k_row = tid >> 3;
-  const int k_col = (((tid & 7) ^ ((k_row >> 1) & 7)) << 4);
-  const int v_row = tid >> 2;
-  const int v_col = (((tid & 3) ^ ((v_row >> 2) & 3)) << 4);
+  // The early waves (0-3) issue every tile load: chunk p = i * 256 + tid,
+  // i = 0, 1.  At this tile size the matrix phases are half as long as the
+  // softmax, so loads issued after the barrier would delay the late waves'
+  // softmax, the longer phase; the early waves carry them inside their
+  // matrix phases instead (K_{j+3} during P_j V_j, V_{j+1} during S_j), or
+  // right after the barrier when they skip a tile.
+  constexpr int NTE = 256;
+  int k_row[2], k_col[2], v_row[2], v_col[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pch = i * NTE + (tid & (NTE - 1));
+    k_row[i] = pch >> 3;
+    k_col[i] = (((pch & 7) ^ ((k_row[i] >> 1) & 7)) << 4);
+    v_row[i] = pch >> 2;
+    v_col[i] = (((pch & 3) ^ ((v_row[i] >> 2) & 3)) << 4);
+  }
+  auto dma_k = [&](int j, int slot, int i) __attribute__((always_inline)) {
+    const int key = min(j * BC + k_row[i], len - 1);
+    uint32_t wb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MIATTN_LDS void*)(sK[slot] + wave * 64 * 16));
+    __asm__ volatile("" : "+s"(wb));
+    lds_dma16_m0(kp + (int64_t)key * D + k_col[i], wb + i * NTE * 16);
+  };
+  auto dma_v = [&](int j, int slot, int i) __attribute__((always_inline)) {
+    uint32_t wb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MIATTN_LDS void*)(sV[slot] + wave * 64 * 16));
+    __asm__ volatile("" : "+s"(wb));
+    lds_dma16_m0(vp + (int64_t)j * VTILE + v_row[i] * 64 + v_col[i], wb + i * NTE * 16);
+  };
   auto issue_k = [&](int j, int slot) __attribute__((always_inline)) {
-    const int key = min(j * BC + k_row, len - 1);
-    lds_dma16(kp + (int64_t)key * D + k_col, sK[slot] + wave * 64 * 16);
+    dma_k(j, slot, 0);
+    dma_k(j, slot, 1);
   };
   auto issue_v = [&](int j, int slot) __attribute__((always_inline)) {
-    lds_dma16(vp + (int64_t)j * VTILE + v_row * 64 + v_col, sV[slot] + wave * 64 * 16);
+    dma_v(j, slot, 0);
+    dma_v(j, slot, 1);
   };
   // operand offsets: K row kb*32 + l32, chunks 4 ks + 2 hi + {0, 1}; V^T row
   // db*32 + l32, chunks 2 hi + {0, 1}
@@ -294,19 +318,36 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
 
   f32x16 s[2];
   i32x8 p8;
-  auto mma_s = [&](auto slot_c) __attribute__((always_inline)) {
-    const uint8_t* kt = sK[decltype(slot_c)::value];
+  auto mma_s = [&](auto slot_c, int j) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint8_t* kt = sK[SL];
+    const bool ld = !late && j + 1 < ntiles;
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_fp8(read32(kt, koff[kb][ks]), qf[ks], s[kb]);
+      if (ld) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_v(j + 1, (SL + 1) % 3, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
-  auto mma_pv = [&](auto slot_c) __attribute__((always_inline)) {
-    const uint8_t* vt = sV[decltype(slot_c)::value];
+  auto mma_pv = [&](auto slot_c, int j) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint8_t* vt = sV[SL];
+    const bool ld = !late && j + 3 < ntiles;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = mfma_fp8(read32(vt, voff[db]), p8, o[db]);
+    for (int db = 0; db < DB; ++db) {
+      o[db] = mfma_fp8(read32(vt, voff[db]), p8, o[db]);
+      if (ld && (db % (DB / 2)) == DB / 2 - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_k(j + 3, SL, db / (DB / 2));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kt0 = j * BC;
@@ -364,31 +405,45 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
     }
   };
 
-  auto begin_interval = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) issue_k(t + 2, (t + 2) % 3);
-    if (t + 1 < ntiles) issue_v(t + 1, (t + 1) % 3);
-  };
+  // Interval t loads K_{t+2} and V_{t+1}; the barrier ending interval t
+  // needs interval t-1's loads (K_{t+1}, V_t) and lets interval t's stay in
+  // flight.  The late waves hold no loads.
+  auto live = [&](int j) __attribute__((always_inline)) -> bool { return j >= 0 && j <= jw_last; };
   auto end_interval = [&](int t) __attribute__((always_inline)) {
-    const int pending = (t + 2 < ntiles ? 1 : 0) + (t + 1 < ntiles ? 1 : 0);
-    if (pending == 2) barrier_vmem_n<2>();
-    else if (pending == 1) barrier_vmem_n<1>();
-    else barrier_vmem_n<0>();
-    begin_interval(t + 1);
+    if (!late) {
+      const int pending = (t + 2 < ntiles ? 2 : 0) + (t + 1 < ntiles ? 2 : 0);
+      if (pending == 4) barrier_vmem_n<4>();
+      else if (pending == 2) barrier_vmem_n<2>();
+      else barrier_vmem_n<0>();
+      if (!live(t) && t + 3 < ntiles) issue_k(t + 3, (t + 3) % 3);
+      if (!live(t + 1) && t + 2 < ntiles) issue_v(t + 2, (t + 2) % 3);
+    } else {
+      barrier_vmem_n<0>();
+    }
   };
 
-  issue_k(0, 0);
-  if (ntiles > 1) issue_k(1, 1);
-  issue_v(0, 0);
-  if (ntiles > 1) barrier_vmem_n<2>();  // K_0 has landed
-  else barrier_vmem_n<1>();
-  begin_interval(0);
+  // Prologue (early waves): K_0, K_1, V_0 and interval 0's K_2 (no P V
+  // precedes S_0); K_0 must land.
+  if (!late) {
+    issue_k(0, 0);
+    if (ntiles > 1) issue_k(1, 1);
+    issue_v(0, 0);
+    if (ntiles > 2) issue_k(2, 2);
+    const int pending = (ntiles > 1 ? 2 : 0) + 2 + (ntiles > 2 ? 2 : 0);
+    if (pending == 6) barrier_vmem_n<6>();
+    else if (pending == 4) barrier_vmem_n<4>();
+    else barrier_vmem_n<2>();
+    if (!live(0) && ntiles > 1) issue_v(1, 1);
+  } else {
+    barrier_vmem_n<0>();
+  }
 
   auto body = [&](int j, auto slot_c) __attribute__((always_inline)) {
-    mma_s(slot_c);
+    mma_s(slot_c, j);
     if (late) end_interval(j);
     softmax(j);
     if (!late) end_interval(j);
-    mma_pv(slot_c);
+    mma_pv(slot_c, j);
   };
   for (int j = 0; j <= jw_last; j += 3) {
     body(j, std::integral_constant<int, 0>{});
