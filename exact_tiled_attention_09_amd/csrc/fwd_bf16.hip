@@ -201,20 +201,26 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
 #pragma unroll
     for (int i = 0; i < LPT; ++i) dma(src, dst, k0, i);
   };
+  // Key-validity flags of a tile, by wave 0.  The raw byte is loaded early
+  // and converted only when stored: a use right after the load would make
+  // the compiler wait there for every load in flight (vmcnt(0)), the tile
+  // loads issued just before it included.
   uint32_t rvalid = 1u;
+  int rkey = 0;
   auto load_flags = [&](int j) __attribute__((always_inline)) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        const int key = j * BC + lane;
-        rvalid = (key < kv_len) ? (uint32_t)(a.key_valid[sv.tok0 + key] != 0) : 1u;
+        rkey = j * BC + lane;
+        rvalid = a.key_valid[sv.tok0 + min(rkey, kv_len - 1)];
       }
     }
   };
   auto store_flags = [&](int j) __attribute__((always_inline)) {
     if constexpr (KPAD) {
       if (wave == 0) {
-        s_valid[j & 3][lane] = (uint8_t)rvalid;
-        const bool any = wave_any(rvalid == 0u);
+        const uint32_t ok = (rkey >= kv_len || rvalid != 0u) ? 1u : 0u;  // keys past the end are masked anyway
+        s_valid[j & 3][lane] = (uint8_t)ok;
+        const bool any = wave_any(ok == 0u);
         if (lane == 0) s_anypad[j & 3] = any ? 1u : 0u;
       }
     }
