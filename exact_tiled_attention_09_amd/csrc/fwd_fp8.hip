@@ -205,6 +205,12 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
 
   __shared__ __attribute__((aligned(16))) uint8_t sK[3][KTILE];
   __shared__ __attribute__((aligned(16))) uint8_t sV[3][VTILE];
+  // The per-tile K scales of the sequence, read once into LDS: read from
+  // memory inside the key loop, each would make the compiler wait for every
+  // load in flight there (it does not count the hand-issued tile loads).
+  // Sequences of more tiles than the table holds read them from memory.
+  constexpr int KSC_CAP = 2048;  // 64-key tiles (N <= 131072)
+  __shared__ float s_ksc[KSC_CAP];
 
   int bh, tile;
   wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);
@@ -254,6 +260,12 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   const int kv_end = CAUSAL ? min(len, q_tile0 + BR) : len;
   const int ntiles = (kv_end + BC - 1) / BC;
   const int jw_last = CAUSAL ? min(ntiles - 1, (q_wave0 + 31) / BC) : ntiles - 1;
+  // The K scales of the tiles this workgroup visits, before any tile load (so
+  // the wait for them waits for nothing else); the prologue's barrier
+  // publishes them.
+  const bool ksc_lds = ntiles <= KSC_CAP;
+  if (ksc_lds)
+    for (int i = tid; i < ntiles; i += NW * 64) s_ksc[i] = ksc[i];
 
   // Direct loads: one 16-byte chunk per thread per tile and tensor.  K tile
   // rows are 128 bytes (8 chunks, chunk c of row r stored at c ^ (r/2 % 8));
@@ -351,7 +363,12 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   };
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int kt0 = j * BC;
-    const float c = c_q * ksc[j];
+    // the LDS read unconditionally and the memory read volatile: otherwise
+    // the compiler merges the two into one flat load of a selected address,
+    // which it then waits for like a memory load on every tile
+    float ks = s_ksc[min(j, KSC_CAP - 1)];
+    if (!ksc_lds) ks = *(const volatile float*)(ksc + j);
+    const float c = c_q * ks;
     bool need_mask = kt0 + BC > len;
     if (CAUSAL) need_mask = need_mask || (kt0 + BC - 1 > q_wave0);
     float cc = c;
