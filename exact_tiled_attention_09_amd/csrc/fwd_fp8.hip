@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
   };
 
   f32x16 s[2];
-  i32x8 p8;
+  i32x8 p8 = {};
   auto mma_s = [&](auto slot_c, int j) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_c)::value;
     const uint8_t* kt = sK[SL];
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
     // exp2 returns P * 2^6 directly (the scaling folded into the exponent);
     // l then carries the same factor, removed exactly in the epilogue
     const float mu = dead ? 0.f : m_new - kPScaleLog2;
-    float rs = 0.f;
+    float rs = -0.f;  // -0 + x == x: the first add folds away
     uint32_t w[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -409,7 +409,10 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Args a, int n_qtiles
           e[i] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + i], cc, -mu));
           rs += e[i];
         }
-        uint32_t x = cvt_fp8x2<false>(e[0], e[1], 0u);
+        // the old word's low half is replaced here and its high half by
+        // the second conversion: passing the previous tile's word (dead by
+        // now) saves clearing a register
+        uint32_t x = cvt_fp8x2<false>(e[0], e[1], (uint32_t)p8[kb * 4 + q4]);
         w[kb * 4 + q4] = cvt_fp8x2<true>(e[2], e[3], x);
       }
     p8 = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
