@@ -29,7 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import gqa_forward, visible_mask
+from .attention import gqa_forward, head_forward, visible_mask
 
 __all__ = [
     "E4M3_MAX",
@@ -40,6 +40,7 @@ __all__ = [
     "dequantize_rows",
     "dequantize_heads",
     "fp8_reference",
+    "fp8_reference_rows",
     "fp8_output_bound",
 ]
 
@@ -138,7 +139,22 @@ def fp8_reference(q, k, v, scale, causal=False):
             "qd": qd, "kd": kd, "vd": vd}
 
 
-def fp8_output_bound(qd, kd, vd, lse, scale, causal=False, p_scale_log2=0):
+def fp8_reference_rows(q, k, v, scale, causal, rows):
+    """fp8_reference for the query positions ``rows`` only, of one head per
+    K/V head: q [1, 1, N, d], k and v [1, 1, N, d].  The whole tensors are
+    quantized (the scales depend on every row of a block); exact attention
+    is then formed for the listed rows alone, so N may be far larger than
+    the full score matrix allows.  Returns dict with o [1, 1, R, d] and lse
+    [1, 1, R] (fp64) and the dequantized tensors."""
+    q8, sq = quantize_rows(q)
+    k8, sk = quantize_rows(k)
+    v8, sv = quantize_heads(v)
+    qd, kd, vd = dequantize_rows(q8, sq), dequantize_rows(k8, sk), dequantize_heads(v8, sv)
+    o, lse = head_forward(qd[0, 0], kd[0, 0], vd[0, 0], scale, causal, rows=np.asarray(rows))
+    return {"o": o[None, None], "lse": lse[None, None], "qd": qd, "kd": kd, "vd": vd}
+
+
+def fp8_output_bound(qd, kd, vd, lse, scale, causal=False, p_scale_log2=0, rows=None):
     """Per-element bound on |O_fp8 - O_ref| from rounding P to E4M3 for the
     P V product, P being multiplied by 2^p_scale_log2 before rounding (and
     divided by it afterwards; p_scale_log2 = 0: no pre-scale).  A P_ij whose
@@ -147,16 +163,20 @@ def fp8_output_bound(qd, kd, vd, lse, scale, causal=False, p_scale_log2=0):
     most half the subnormal step, 2^-10 / 2^p_scale_log2, and never by more
     than itself.  The error of O_i is at most
     sum_j min(P_ij, max(2^-4 P_ij, 2^-10 / 2^p_scale_log2)) |V_j|.
-    Returns (bound, weighted) [B, H, N, d] fp64, weighted = sum_j P_ij |V_j|."""
+    Returns (bound, weighted) [B, H, N, d] fp64, weighted = sum_j P_ij |V_j|.
+    With ``rows`` (query positions) only those rows are formed: lse is then
+    [B, H, len(rows)] and both results [B, H, len(rows), d] (for sequences
+    too long for the whole N x N score matrix)."""
     B, H, N, d = qd.shape
     G = H // kd.shape[1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
     floor_ = 2.0 ** -10 / 2.0 ** p_scale_log2
-    bound = np.zeros(qd.shape)
-    weighted = np.zeros(qd.shape)
+    bound = np.zeros((B, H, len(rows), d))
+    weighted = np.zeros((B, H, len(rows), d))
     for b in range(B):
         for h in range(H):
-            s = scale * (qd[b, h] @ kd[b, h // G].T)
-            s = np.where(visible_mask(np.arange(N), N, causal), s, -np.inf)
+            s = scale * (qd[b, h][rows] @ kd[b, h // G].T)
+            s = np.where(visible_mask(rows, N, causal), s, -np.inf)
             p = np.exp(s - lse[b, h][:, None])
             dp = np.minimum(p, np.maximum(2.0 ** -4 * p, floor_))
             bound[b, h] = dp @ np.abs(vd[b, h // G])

@@ -225,3 +225,34 @@ def test_fp8_full_size_causal(lib):
         _say(f"oracle head b={b} h={h}")
         sl = (slice(b, b + 1), slice(h, h + 1))
         _check(o[sl], lse[sl], inp["q"][sl], inp["k"][sl], inp["v"][sl], scale, True, mse_bar=1e-4)
+
+
+def test_fp8_key_scales_past_the_lds_table(lib):
+    """One sequence longer than the forward's LDS table of per-tile K scales
+    (2048 tiles of 64 keys): B1 H1 N 131264 (2051 key tiles), causal.  The
+    query tile at row 130816 visits exactly 2048 key tiles (the table's
+    last entry); the tiles from row 131072 on visit 2051 and read their K
+    scales from memory.  Sampled rows on both sides of that limit, and early
+    rows, against the oracle's row-restricted FP8 reference and bound."""
+    N = 131264
+    _say(f"fp8 N={N}: generate")
+    inp = dense_inputs(1, 1, N, 128, "bf16", seed=5, with_do=False)
+    scale = 1 / math.sqrt(128)
+    o, lse = _fwd(lib, inp["q"], inp["k"], inp["v"], scale, True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = np.array([0, 1, 4095, 65536, 130815, 130816, 131000, 131071, 131072, 131073, 131200, N - 2, N - 1])
+    _say("oracle rows")
+    ref = F.fp8_reference_rows(inp["q"], inp["k"], inp["v"], scale, True, rows)
+    bound, weighted = F.fp8_output_bound(ref["qd"], ref["kd"], ref["vd"], ref["lse"], scale, True,
+                                         p_scale_log2=_P_SCALE_LOG2, rows=rows)
+    a_ = np.abs(ref["qd"][0, 0][rows]) @ np.abs(ref["kd"][0, 0]).T
+    a_ = np.where(np.arange(N)[None, :] <= rows[:, None], a_, 0.0)
+    delta = 2.0 ** -12 * abs(scale) * a_.max(axis=1)       # [R], the accumulation term of _check
+    got_o, got_lse = o[0, 0][rows], lse[0, 0][rows]
+    allowed = bound[0, 0] + (2.0 ** -8 + delta[:, None]) * weighted[0, 0] + 2.0 ** -8 * np.abs(ref["o"][0, 0])
+    worst = np.max(np.abs(got_o - ref["o"][0, 0]) - allowed)
+    _say(f"  worst O margin {worst:.3e}")
+    assert worst <= 0, f"O outside the FP8 bound by {worst:.3e}"
+    lerr = np.abs(got_lse - ref["lse"][0, 0]) - (1e-3 + delta)
+    _say(f"  LSE worst margin {lerr.max():.3e}")
+    assert lerr.max() <= 0

@@ -9,7 +9,9 @@
   error of every normal code is at most 2^-4, all-zero blocks.
 * The FP8 reference equals exact attention when quantization is lossless,
   and the error bound covers an explicit simulation of rounding P to E4M3,
-  with and without a power-of-two pre-scale of P."""
+  with and without a power-of-two pre-scale of P.
+* The row-restricted reference and bound equal the whole-head ones on the
+  rows they form."""
 import os
 import types
 
@@ -109,6 +111,26 @@ def test_lossless_quantization_gives_exact_attention():
     o, lse = A.gqa_forward(q, k, v, 0.05, causal=True)
     np.testing.assert_allclose(ref["o"], o, rtol=0, atol=1e-12)
     np.testing.assert_allclose(ref["lse"], lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_forms_equal_the_whole_head_forms(causal):
+    """fp8_reference_rows and fp8_output_bound(rows=...) give, for the listed
+    query positions, exactly the rows of the whole-head reference and bound
+    (the row forms serve sequences too long for the full score matrix)."""
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((1, 1, 200, 16)).astype(np.float32) for _ in range(3))
+    rows = np.array([0, 1, 63, 64, 130, 199])
+    full = F.fp8_reference(q, k, v, 0.3, causal)
+    part = F.fp8_reference_rows(q, k, v, 0.3, causal, rows)
+    # the same arithmetic, up to the rounding order of differently shaped products
+    np.testing.assert_allclose(part["o"], full["o"][:, :, rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(part["lse"], full["lse"][:, :, rows], rtol=1e-12, atol=0)
+    bf, wf = F.fp8_output_bound(full["qd"], full["kd"], full["vd"], full["lse"], 0.3, causal, p_scale_log2=6)
+    bp, wp = F.fp8_output_bound(part["qd"], part["kd"], part["vd"], part["lse"], 0.3, causal, p_scale_log2=6,
+                                rows=rows)
+    np.testing.assert_allclose(bp, bf[:, :, rows], rtol=1e-12, atol=0)
+    np.testing.assert_allclose(wp, wf[:, :, rows], rtol=1e-12, atol=0)
 
 
 @pytest.mark.parametrize("p_log2", [0, 6])
