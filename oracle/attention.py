@@ -39,6 +39,7 @@ __all__ = [
     "head_forward",
     "head_backward",
     "head_backward_sampled",
+    "head_backward_sampled_sparse",
     "forward",
     "backward",
     "varlen_forward",
@@ -68,8 +69,9 @@ def block_table(row_ptr, col_idx, n_qblocks: int, n_kblocks: int) -> np.ndarray:
 
 
 def visible_mask(rows: np.ndarray, n_keys: int, causal: bool, key_valid=None, window=None,
-                 blocks=None) -> np.ndarray:
-    """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend key j.
+                 blocks=None, keys=None) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend key j
+    (``keys``: only those key positions, giving [len(rows), len(keys)]).
 
     Causal: key j is visible to query i iff j <= i [P4 §18.2.2 item 3, M_ij = 0 for
     j <= i].  Key padding: invalid keys are hidden from every query [P4 §18.2.2
@@ -80,12 +82,12 @@ def visible_mask(rows: np.ndarray, n_keys: int, causal: bool, key_valid=None, wi
     listed for query block i // block [P4 §18.8.1, block-sparse FlashAttention:
     blocks that are not listed contribute nothing]."""
     rows = np.asarray(rows)
-    keys = np.arange(n_keys)
-    vis = np.ones((len(rows), n_keys), dtype=bool)
+    keys = np.arange(n_keys) if keys is None else np.asarray(keys)
+    vis = np.ones((len(rows), len(keys)), dtype=bool)
     if causal:
         vis &= keys[None, :] <= rows[:, None]
     if key_valid is not None:
-        vis &= np.asarray(key_valid, dtype=bool)[None, :]
+        vis &= np.asarray(key_valid, dtype=bool)[keys][None, :]
     if window is not None:
         left, right = window
         if left >= 0:
@@ -231,6 +233,60 @@ def head_backward_sampled(q, k, v, do, scale, causal=False, key_valid=None, quer
             dv += p.T @ do[r]
             dk += scale * (ds.T @ q[r])
     return dq, dk, dv, o, lse, dvec
+
+
+def head_backward_sampled_sparse(q, k, v, do, scale, causal=False, key_valid=None, query_rows=(), key_cols=(),
+                                 row_chunk=4096, window=None, blocks=None):
+    """head_backward_sampled for a sequence too long for a forward over every
+    row: dQ, O and LSE at ``query_rows`` and dK, dV at ``key_cols``.  O, LSE
+    and D are formed only for the rows that matter: the query rows
+    themselves and every row that sees one of the key columns.  A row that
+    sees none of them adds exact zeros to their dK and dV.  The definition is
+    that of ``head_backward``, so the results equal head_backward_sampled's
+    up to the order of rounding.  Cheap when the mask (a window, a block
+    list) leaves each sampled column to few rows.
+    Returns (dQ, dK, dV, O at query_rows, LSE at query_rows), fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, n_keys = q.shape[0], k.shape[0]
+    rows = np.asarray(query_rows, dtype=np.int64)
+    cols = np.asarray(key_cols, dtype=np.int64)
+    seen = [np.zeros(0, np.int64)]
+    if len(cols):
+        for c0 in range(0, n, row_chunk):
+            r = np.arange(c0, min(n, c0 + row_chunk))
+            vis = visible_mask(r, n_keys, causal, key_valid, window, blocks, keys=cols)
+            seen.append(r[vis.any(axis=1)])
+    need = np.union1d(np.concatenate(seen), rows).astype(np.int64)
+    o, lse = head_forward(q, k, v, scale, causal, key_valid, rows=need, row_chunk=row_chunk, window=window,
+                          blocks=blocks)
+    dvec = np.sum(do[need] * o, axis=1)
+    at = np.searchsorted(need, rows)
+    dq = np.zeros((len(rows), q.shape[1]))
+    if len(rows):
+        s = _scores(q[rows], k, scale, visible_mask(rows, n_keys, causal, key_valid, window, blocks))
+        dead = ~np.isfinite(lse[at])
+        p = np.where(dead[:, None], 0.0, np.exp(s - np.where(dead, 0.0, lse[at])[:, None]))
+        dp = do[rows] @ v.T
+        ds = p * (dp - dvec[at][:, None])
+        dq = scale * (ds @ k)
+    dk = np.zeros((len(cols), k.shape[1]))
+    dv = np.zeros((len(cols), v.shape[1]))
+    if len(cols):
+        for c0 in range(0, len(need), row_chunk):
+            sel = np.arange(c0, min(len(need), c0 + row_chunk))
+            r = need[sel]
+            vis = visible_mask(r, n_keys, causal, key_valid, window, blocks, keys=cols)
+            s = np.where(vis, scale * (q[r] @ k[cols].T), -np.inf)
+            dead = ~np.isfinite(lse[sel])
+            p = np.where(dead[:, None], 0.0, np.exp(s - np.where(dead, 0.0, lse[sel])[:, None]))
+            dp = do[r] @ v[cols].T
+            ds = p * (dp - dvec[sel][:, None])
+            dv += p.T @ do[r]
+            dk += scale * (ds.T @ q[r])
+    return dq, dk, dv, o[at], lse[at]
 
 
 def preprocess_d(o, do):

@@ -11,7 +11,8 @@ calls.  At full size: a sliding window of 4096 keys over N = 16384 and a
 global + local + strided block list over N = 16384, both with 32 query heads
 on 8 key/value heads: every output finite, and one key/value group against
 the oracle (O and LSE of its query heads whole, dQ at sampled query rows, dK
-and dV at sampled key columns)."""
+and dV at sampled key columns).  At the block list's limit: N = 131072 with a
+query block listing all 1024 key blocks, on sampled rows and columns."""
 import math
 import time
 
@@ -277,3 +278,43 @@ def test_block_sparse_cut_key_blocks(lib, causal):
         assert torch.equal(out[name], out2[name]), name
     ref = A.gqa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, blocks=(rp, ci, BLOCK))
     _check(out, ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_longest_lists(lib, causal):
+    """The largest block list the entry points take: N = 131072 (1024 blocks
+    of 128), B1 H2 on one K/V head, d = 64.  Query block r lists r-1, r, r+1
+    and every 128th block (block 0 included); the last query block lists all
+    1024, the longest list there can be.  O, LSE and dQ at sampled rows (the
+    first and last rows of the sequence and of the longest list's block among
+    them) and dK, dV at key columns of blocks that only their neighbours and
+    the last query block list, summed over the two query heads, against the
+    oracle's row-sparse sampled backward."""
+    _say(f"block-sparse longest lists causal={causal}: generate")
+    B, H, Hkv, N, d = 1, 2, 1, 131072, 64
+    nb = N // BLOCK
+    strided = set(range(0, nb, 128))
+    rows_ = [sorted({c for c in (r - 1, r, r + 1) if 0 <= c < nb} | strided) for r in range(nb - 1)]
+    rows_.append(list(range(nb)))
+    rp, ci = _csr(rows_)
+    inp = dense_inputs(B, H, N, d, "bf16", seed=41, kv_heads=Hkv)
+    scale = 1 / math.sqrt(d)
+    out = _run_sparse(lib, inp, scale, causal, rp, ci)
+    rng = np.random.default_rng(41)
+    rows = np.sort(np.concatenate([[0, 1, 500 * BLOCK + 5, (nb - 1) * BLOCK, N - 2, N - 1],
+                                   rng.choice(N, 10, replace=False)]))
+    cols = np.array([5 * BLOCK + 7, 300 * BLOCK + 64, 1000 * BLOCK + 127, (nb - 1) * BLOCK, N - 1])
+    dk_sum = np.zeros((len(cols), d))
+    dv_sum = np.zeros_like(dk_sum)
+    for h in range(H):
+        _say(f"oracle head {h}, row-sparse sampled")
+        dq, dk, dv, o, lse = A.head_backward_sampled_sparse(inp["q"][0, h], inp["k"][0, 0], inp["v"][0, 0],
+                                                            inp["do"][0, h], scale, causal, None, rows, cols,
+                                                            blocks=(rp, ci, BLOCK))
+        check_bf16(to_np(out["o"][0, h])[rows], o, f"O[{h}] rows", max_abs_tol=BF16_O_MAX_ABS)
+        check_lse(to_np(out["lse"][0, h])[rows], lse)
+        check_bf16(to_np(out["dq"][0, h])[rows], dq, f"dq[{h}] rows")
+        dk_sum += dk
+        dv_sum += dv
+    check_bf16(to_np(out["dk"][0, 0])[cols], dk_sum, "dk cols")
+    check_bf16(to_np(out["dv"][0, 0])[cols], dv_sum, "dv cols")

@@ -390,6 +390,38 @@ def test_sampled_backward_matches_full_backward(causal):
     np.testing.assert_allclose(so, o, atol=1e-14)
 
 
+@pytest.mark.parametrize("mask", ["causal", "padded", "window", "blocks"])
+def test_row_sparse_sampled_backward_matches_full_backward(mask):
+    """The row-sparse sampled form (O, LSE, D only for the rows that need
+    them) picks the same entries out of the full backward under every mask,
+    with a row chunk smaller than the problem so that rows are skipped."""
+    rng = np.random.default_rng(21)
+    n, d = 300, 6
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    kw = {"causal": mask in ("causal", "blocks")}
+    if mask == "padded":
+        kv = np.ones(n, np.uint8)
+        kv[[0, 7, 130, 299]] = 0
+        kw["key_valid"] = kv
+    if mask == "window":
+        kw["window"] = (20, 3)
+    if mask == "blocks":
+        rows_ = [[0, r] if r != 2 else [0, 1, 2] for r in range(3)]
+        kw["blocks"] = (np.array([0, 2, 4, 7]), np.array([c for r in rows_ for c in r]), 128)
+    rows = [0, 3, 127, 128, 200, 299]
+    cols = [1, 150, 160, 260, 299]
+    dq, dk, dv, o, lse, _ = A.head_backward(q, k, v, g, 0.4, row_chunk=64, **kw)
+    sq, sk, sv_, so, sl = A.head_backward_sampled_sparse(q, k, v, g, 0.4, query_rows=rows, key_cols=cols,
+                                                         row_chunk=50, **kw)
+    np.testing.assert_allclose(sq, dq[rows], atol=1e-12)
+    np.testing.assert_allclose(sk, dk[cols], atol=1e-12)
+    np.testing.assert_allclose(sv_, dv[cols], atol=1e-12)
+    np.testing.assert_allclose(so, o[rows], atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(sl), np.isneginf(lse[rows]))
+    fin = np.isfinite(lse[rows])
+    np.testing.assert_allclose(sl[fin], lse[rows][fin], atol=1e-13)
+
+
 def test_preprocess_d_pins():
     """The pre-pass alone: D = rowsum(dO o O) [P1 §5.2].  Pinned to the other
     form of the same quantity, rowsum(P o dP), which head_backward checks
