@@ -67,6 +67,7 @@ CASES = [
     (2, 6, 3, 300, 64, [299, 300]),
     (3, 12, 12, 777, 128, [0, 0, 777]),
     (1, 40, 8, 70000, 128, [65537]),
+    (1, 8, 1, 1 << 20, 64, [1048000]),  # a 2^20-token cache: 1024 pieces to merge
 ]
 
 

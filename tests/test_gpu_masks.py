@@ -318,3 +318,32 @@ def test_block_sparse_longest_lists(lib, causal):
         dv_sum += dv
     check_bf16(to_np(out["dk"][0, 0])[cols], dk_sum, "dk cols")
     check_bf16(to_np(out["dv"][0, 0])[cols], dv_sum, "dv cols")
+
+
+def test_window_long_sequence(lib):
+    """A causal window of 128 keys over N = 131072, B1 H2 on one K/V head,
+    d = 64: O, LSE and dQ at sampled rows and dK, dV at sampled key columns
+    (summed over the two query heads) against the oracle's row-sparse
+    sampled backward."""
+    _say("window over N = 131072: generate")
+    B, H, Hkv, N, d = 1, 2, 1, 131072, 64
+    inp = dense_inputs(B, H, N, d, "bf16", seed=43, kv_heads=Hkv)
+    scale = 1 / math.sqrt(d)
+    out = _run_window(lib, inp, scale, True, 127, 0)
+    rng = np.random.default_rng(43)
+    rows = np.sort(np.concatenate([[0, 1, 127, 128, N - 2, N - 1], rng.choice(N, 10, replace=False)]))
+    cols = np.sort(np.concatenate([[0, 1, N - 129, N - 1], rng.choice(N, 6, replace=False)]))
+    dk_sum = np.zeros((len(cols), d))
+    dv_sum = np.zeros_like(dk_sum)
+    for h in range(H):
+        _say(f"oracle head {h}, row-sparse sampled")
+        dq, dk, dv, o, lse = A.head_backward_sampled_sparse(inp["q"][0, h], inp["k"][0, 0], inp["v"][0, 0],
+                                                            inp["do"][0, h], scale, True, None, rows, cols,
+                                                            window=(127, 0))
+        check_bf16(to_np(out["o"][0, h])[rows], o, f"O[{h}] rows", max_abs_tol=BF16_O_MAX_ABS)
+        check_lse(to_np(out["lse"][0, h])[rows], lse)
+        check_bf16(to_np(out["dq"][0, h])[rows], dq, f"dq[{h}] rows")
+        dk_sum += dk
+        dv_sum += dv
+    check_bf16(to_np(out["dk"][0, 0])[cols], dk_sum, "dk cols")
+    check_bf16(to_np(out["dv"][0, 0])[cols], dv_sum, "dv cols")
