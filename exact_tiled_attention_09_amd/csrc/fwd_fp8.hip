@@ -59,6 +59,25 @@ __device__ __forceinline__ float wave_max64(float x) {
 }
 
 // ------------------------------------------------------------------ quantizers
+// x / s rounded to nearest, as the fp32 division gives it, for one scale s of
+// a whole block: Markstein's correction of a reciprocal product (IBM RISC
+// System/6000, 1990).  With y = RN(1/s) formed once, q = RN(x y) lies within
+// an ulp of x / s, the remainder r = x - s q is exact in one fma, and
+// RN(q + r y) = RN(x / s) as long as nothing underflows; so scales outside
+// [2^-60, 2^60] keep the division.  A zero quotient takes x's sign, as the
+// division's does.  Three instructions instead of the division's sequence.
+struct DivByScale {
+  float s, y;
+  bool fast;
+  __device__ __forceinline__ explicit DivByScale(float s_) : s(s_), y(1.f / s_), fast(s_ >= 0x1p-60f && s_ <= 0x1p60f) {}
+  __device__ __forceinline__ float operator()(float x) const {
+    if (!fast) return x / s;
+    const float q = x * y;
+    const float r = __builtin_fmaf(-q, s, x);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+  }
+};
+
 struct QuantArgs {
   const uint16_t* x;   // bf16 [B*H, N, D]
   uint8_t* x8;         // codes
@@ -99,15 +118,16 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a, int nb) {
   amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
   const float s = amax == 0.f ? 1.f : amax / kFp8Max;
   if (tid == 0) a.scales[(int64_t)bh * nb + t] = s;
+  const DivByScale div(s);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = i * 256 + tid;
     if (c * 8 < rows * D) {
       uint32_t lo = 0u, hi = 0u;
-      lo = cvt_fp8x2<false>(bf16_bits_to_f32(raw[i][0] & 0xffffu) / s, bf16_bits_to_f32(raw[i][0] >> 16) / s, lo);
-      lo = cvt_fp8x2<true>(bf16_bits_to_f32(raw[i][1] & 0xffffu) / s, bf16_bits_to_f32(raw[i][1] >> 16) / s, lo);
-      hi = cvt_fp8x2<false>(bf16_bits_to_f32(raw[i][2] & 0xffffu) / s, bf16_bits_to_f32(raw[i][2] >> 16) / s, hi);
-      hi = cvt_fp8x2<true>(bf16_bits_to_f32(raw[i][3] & 0xffffu) / s, bf16_bits_to_f32(raw[i][3] >> 16) / s, hi);
+      lo = cvt_fp8x2<false>(div(bf16_bits_to_f32(raw[i][0] & 0xffffu)), div(bf16_bits_to_f32(raw[i][0] >> 16)), lo);
+      lo = cvt_fp8x2<true>(div(bf16_bits_to_f32(raw[i][1] & 0xffffu)), div(bf16_bits_to_f32(raw[i][1] >> 16)), lo);
+      hi = cvt_fp8x2<false>(div(bf16_bits_to_f32(raw[i][2] & 0xffffu)), div(bf16_bits_to_f32(raw[i][2] >> 16)), hi);
+      hi = cvt_fp8x2<true>(div(bf16_bits_to_f32(raw[i][3] & 0xffffu)), div(bf16_bits_to_f32(raw[i][3] >> 16)), hi);
       *(u32x2*)(dst + c * 8) = u32x2{lo, hi};
     }
   }
@@ -175,17 +195,17 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(QuantArgs a, int nt) {
     *(u32x4*)(tile + r * LD + col) = v;
   }
   __syncthreads();
-  const float s = a.scales[bh];
+  const DivByScale div(a.scales[bh]);
   uint8_t* dst = a.x8 + ((int64_t)bh * nt + t) * (int64_t)D * 64;
   // one output word = 4 consecutive positions p0..p0+3 = keys k(p0)..k(p0)+3
   for (int w = tid; w < D * 16; w += 256) {
     const int f = w >> 4;
     const int p0 = (w & 15) * 4;
     const int k0 = 32 * ((p0 % 32) / 16) + 8 * ((p0 % 16) / 4) + 4 * (p0 / 32);
-    const float x0 = bf16_bits_to_f32(tile[(k0 + 0) * LD + f]) / s;
-    const float x1 = bf16_bits_to_f32(tile[(k0 + 1) * LD + f]) / s;
-    const float x2 = bf16_bits_to_f32(tile[(k0 + 2) * LD + f]) / s;
-    const float x3 = bf16_bits_to_f32(tile[(k0 + 3) * LD + f]) / s;
+    const float x0 = div(bf16_bits_to_f32(tile[(k0 + 0) * LD + f]));
+    const float x1 = div(bf16_bits_to_f32(tile[(k0 + 1) * LD + f]));
+    const float x2 = div(bf16_bits_to_f32(tile[(k0 + 2) * LD + f]));
+    const float x3 = div(bf16_bits_to_f32(tile[(k0 + 3) * LD + f]));
     uint32_t word = cvt_fp8x2<false>(x0, x1, 0u);
     word = cvt_fp8x2<true>(x2, x3, word);
     *(uint32_t*)(dst + f * 64 + p0) = word;

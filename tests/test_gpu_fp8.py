@@ -94,6 +94,46 @@ def test_quantizers_bit_exact(lib, N, sigma):
     np.testing.assert_array_equal(vscales.cpu().numpy().view(np.uint32), hs.view(np.uint32))
 
 
+def _every_bf16_by_maximum():
+    """[1, H, 512, 128] bf16-exact inputs: head h holds a maximum M_h first,
+    then every finite bf16 value of magnitude at most M_h (in bit order, so
+    the 64-row blocks see many different maxima), then zeros.  The maxima
+    run from subnormal bf16 numbers (scales far below 2^-60) to the largest
+    finite bf16 (a scale near 2^120), with powers of two and values between."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = bits[(bits & 0x7F80) != 0x7F80]
+    vals = (finite << 16).view(np.float32)
+    maxima = [float(np.array([b << 16], np.uint32).view(np.float32)[0])
+              for b in (0x0001, 0x007F, 0x0080, 0x0D00, 0x1A55, 0x2000, 0x3000, 0x3A80, 0x3C00, 0x3F80,
+                        0x3FC1, 0x4100, 0x4388, 0x4500, 0x5000, 0x5E00, 0x6A12, 0x7000, 0x7F00, 0x7F7F)]
+    x = np.zeros((1, len(maxima), 512, 128), np.float32)
+    for h, m in enumerate(maxima):
+        keep = vals[np.abs(vals) <= m]
+        flat = np.concatenate([[m], keep])
+        assert flat.size <= 512 * 128
+        x[0, h].reshape(-1)[:flat.size] = flat
+    return x
+
+
+def test_quantizers_every_bf16_value(lib):
+    """Both quantizers, bit for bit against the oracle, on every finite bf16
+    value (both zeros and the subnormals included) under twenty head and
+    block maxima, so the codes and scales cover the whole E4M3 range and
+    both ways the kernels divide by a scale."""
+    import torch
+    x = _every_bf16_by_maximum()
+    codes, scales = _quant(lib, x)
+    vcodes, vscales = _quant(lib, x, vt=True)
+    torch.cuda.synchronize()
+    rc, rs = F.quantize_rows(x)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    hc, hs = F.quantize_heads(x)
+    np.testing.assert_array_equal(vscales.cpu().numpy().view(np.uint32), hs.view(np.uint32))
+    got, _ = _untile_vt(vcodes.cpu().numpy(), x.shape[2])
+    np.testing.assert_array_equal(got, hc)
+
+
 # The order attn_quantize_fp8_vt declares in include/miattn.h: position p of a
 # 64-key tile holds key k(p) of the tile.
 _VT_KEY_OF_POS = np.array([32 * ((p % 32) // 16) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
