@@ -927,6 +927,7 @@ def main(argv=None):
     per = {k_: v_ for k_, v_ in per.items() if v_}
     mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
     med = {k_: statistics.median(v_) for k_, v_ in per.items()}
+    low = {k_: min(v_) for k_, v_ in per.items()}
 
     f_fwd, f_bwd = workload_flops(cfg)
     ms_step = wall * 1e3 / args.steps
@@ -938,7 +939,8 @@ def main(argv=None):
 
     by = kernel_bytes(B, H, Hkv, N, d)
     gbps = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)  # noqa: E731
-    bwd = {"ms": round(bwd_ms, 4), "tflops": round(tflops_bwd, 2),
+    bwd = {"ms": round(bwd_ms, 4), "ms_median": round(med["bwd"], 4), "ms_min": round(low["bwd"], 4),
+           "tflops": round(tflops_bwd, 2),
            "pct_mfma_peak": round(100 * tflops_bwd / PEAK_BF16_TFLOPS, 2), "gbps": gbps(by["bwd"], bwd_ms)}
     # dominant kernel for the roofline: the longest of the MFMA kernels whose
     # launches the events bracket one by one
@@ -946,9 +948,11 @@ def main(argv=None):
     if not grouped:
         tflops_dkdv = f_dkdv / (mean["bwd_dkdv"] * 1e-3) / 1e12
         tflops_dq = f_dq / (mean["bwd_dq"] * 1e-3) / 1e12
-        bwd.update({"dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
+        bwd.update({"dkdv_ms": round(mean["bwd_dkdv"], 4), "dkdv_ms_median": round(med["bwd_dkdv"], 4),
+                    "dkdv_ms_min": round(low["bwd_dkdv"], 4), "dkdv_tflops": round(tflops_dkdv, 2),
                     "dkdv_gbps": gbps(by["dkdv"], mean["bwd_dkdv"]),
-                    "dq_ms": round(mean["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2),
+                    "dq_ms": round(mean["bwd_dq"], 4), "dq_ms_median": round(med["bwd_dq"], 4),
+                    "dq_ms_min": round(low["bwd_dq"], 4), "dq_tflops": round(tflops_dq, 2),
                     "dq_gbps": gbps(by["dq"], mean["bwd_dq"]), "dq_forms_d": True})
         kern["bwd_dkdv_kernel (attn_bwd_dkdv)"] = (mean["bwd_dkdv"], f_dkdv, by["dkdv"])
         kern["bwd_dq_kernel (attn_bwd_dq_preprocess)"] = (mean["bwd_dq"], f_dq, by["dq"])
@@ -981,7 +985,8 @@ def main(argv=None):
                                f"B{B} {heads} N{N} d{d} bf16", "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d,
                    "causal": causal, "scale": scale, "flops_fwd": f_fwd, "flops_bwd": f_bwd,
                    "visible_pairs_per_head": visible_pairs(cfg) if masked else None},
-        "fwd": {"ms": round(mean["fwd"], 4), "ms_median": round(med["fwd"], 4), "tflops": round(tflops_fwd, 2),
+        "fwd": {"ms": round(mean["fwd"], 4), "ms_median": round(med["fwd"], 4), "ms_min": round(low["fwd"], 4),
+                "tflops": round(tflops_fwd, 2),
                 "pct_mfma_peak": round(100 * tflops_fwd / PEAK_BF16_TFLOPS, 2),
                 "gbps": gbps(by["fwd"], mean["fwd"])},
         "bwd": bwd,
