@@ -197,18 +197,24 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(QuantArgs a, int nt) {
   __syncthreads();
   const DivByScale div(a.scales[bh]);
   uint8_t* dst = a.x8 + ((int64_t)bh * nt + t) * (int64_t)D * 64;
-  // one output word = 4 consecutive positions p0..p0+3 = keys k(p0)..k(p0)+3
-  for (int w = tid; w < D * 16; w += 256) {
-    const int f = w >> 4;
-    const int p0 = (w & 15) * 4;
-    const int k0 = 32 * ((p0 % 32) / 16) + 8 * ((p0 % 16) / 4) + 4 * (p0 / 32);
-    const float x0 = div(bf16_bits_to_f32(tile[(k0 + 0) * LD + f]));
-    const float x1 = div(bf16_bits_to_f32(tile[(k0 + 1) * LD + f]));
-    const float x2 = div(bf16_bits_to_f32(tile[(k0 + 2) * LD + f]));
-    const float x3 = div(bf16_bits_to_f32(tile[(k0 + 3) * LD + f]));
-    uint32_t word = cvt_fp8x2<false>(x0, x1, 0u);
-    word = cvt_fp8x2<true>(x2, x3, word);
-    *(uint32_t*)(dst + f * 64 + p0) = word;
+  // 16 consecutive positions p0..p0+15 of one feature per thread and step,
+  // one 16-byte store; each word = 4 positions p..p+3 = keys k(p)..k(p)+3
+  for (int w = tid; w < D * 4; w += 256) {
+    const int f = w >> 2;
+    const int pb = (w & 3) * 16;
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p0 = pb + 4 * j;
+      const int k0 = 32 * ((p0 % 32) / 16) + 8 * ((p0 % 16) / 4) + 4 * (p0 / 32);
+      const float x0 = div(bf16_bits_to_f32(tile[(k0 + 0) * LD + f]));
+      const float x1 = div(bf16_bits_to_f32(tile[(k0 + 1) * LD + f]));
+      const float x2 = div(bf16_bits_to_f32(tile[(k0 + 2) * LD + f]));
+      const float x3 = div(bf16_bits_to_f32(tile[(k0 + 3) * LD + f]));
+      uint32_t word = cvt_fp8x2<false>(x0, x1, 0u);
+      out[j] = cvt_fp8x2<true>(x2, x3, word);
+    }
+    *(u32x4*)(dst + f * 64 + pb) = out;
   }
 }
 
