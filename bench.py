@@ -28,6 +28,13 @@ Other workloads: the D pre-pass alone (attn_bwd_preprocess, HBM-bound),
 decoding against a KV cache (HBM-bound), the FP8 forward, packed
 variable-length sequences with key padding, and the small fp32 problem.
 
+Timing: the step first runs back to back for --settle-ms (default 250 ms)
+of host time, then --warmup untimed steps, then exactly --steps steps
+between two device synchronizations, with no other host work in between.
+Per-kernel times come from HIP events on the library's stream (mean,
+median, minimum); `value` is whole-job throughput over the wall time of the
+timed steps.
+
 The CPU baseline runs the fp64 oracle on the host with its BLAS threads
 pinned to the cores of this process's affinity set (the count reported).
 
@@ -307,6 +314,53 @@ class no_gc:
         return False
 
 
+def settle(step, stream, ms):
+    """Run `step` back to back for `ms` milliseconds before the warm-up.
+
+    Under a steady load the part settles to a lower power state than the one
+    it starts a burst in: after even a few milliseconds idle, the next dozen
+    steps of the benchmark workload run 5-30% slower than the steps after
+    them.  The host stays at most four steps ahead (it waits for the event of
+    the step four back), so the queue never drains and the device never idles
+    in between."""
+    if ms <= 0:
+        return
+    import torch
+    pending = []
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        step()
+        e = torch.cuda.Event()
+        e.record(stream)
+        pending.append(e)
+        if len(pending) > 4:
+            pending.pop(0).synchronize()
+
+
+def timed_steps(args, stream, step, n_events):
+    """Settle, warm up, then time exactly `args.steps` steps.
+
+    Events are created and the garbage collector is stopped before the
+    settle phase, so that between the last warm-up step and the first timed
+    one the host only synchronizes: no host work leaves the device idle
+    there.  Returns the per-step event lists and the wall time of the timed
+    steps."""
+    import torch
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(args.steps)]
+    log(f"settle {args.settle_ms} ms, warm up {args.warmup} steps, time {args.steps} steps")
+    with no_gc():
+        settle(step, stream, args.settle_ms)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for ev in events:
+            step(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return events, wall
+
+
 def host_cores() -> int:
     """Cores this process may run on (its CPU affinity set)."""
     return len(os.sched_getaffinity(0))
@@ -393,16 +447,7 @@ def run_fp8(args, cfg):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    with no_gc():
-        t0 = time.perf_counter()
-        for ev in events:
-            step(ev)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    events, wall = timed_steps(args, stream, step, 3)
     q_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
     f_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
     f_fwd, _ = flops(B, H, N, d, causal)
@@ -416,6 +461,7 @@ def run_fp8(args, cfg):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -456,13 +502,15 @@ def run_prep(args, cfg):
     ws = torch.empty(M.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     M.attn_fwd(q, k, v, o, lse, scale, True, stream)
-    for _ in range(args.warmup):
-        M.attn_bwd_preprocess(o, do, ws, stream)
-    torch.cuda.synchronize()
     # one event pair around the back-to-back launches: for a ~40 us kernel a
     # pair around every launch would add its own few microseconds
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"settle {args.settle_ms} ms, warm up {args.warmup} launches, time {args.steps} launches")
     with no_gc():
+        settle(lambda: M.attn_bwd_preprocess(o, do, ws, stream), stream, args.settle_ms)
+        for _ in range(args.warmup):
+            M.attn_bwd_preprocess(o, do, ws, stream)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
         for _ in range(args.steps):
@@ -482,6 +530,7 @@ def run_prep(args, cfg):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -525,18 +574,14 @@ def run_decode(args, cfg):
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(M.attn_decode_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
         M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    with no_gc():
-        t0 = time.perf_counter()
-        for e0, e1 in events:
-            e0.record(stream)
-            M.attn_decode(q, k, v, o, lse, scale, None, ws, stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        if ev is not None:
+            ev[1].record(stream)
+
+    events, wall = timed_steps(args, stream, step, 2)
     ms = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in events)
     nbytes = 2 * B * Hkv * N * d * 2 + 2 * B * H * d * 2 + B * H * 4
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -547,6 +592,7 @@ def run_decode(args, cfg):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -612,18 +658,7 @@ def run_varlen(args, cfg):
         if ev is not None:
             ev[2].record(stream)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    with no_gc():
-        t0 = time.perf_counter()
-        for ev in events:
-            step(ev)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    events, wall = timed_steps(args, stream, step, 3)
     f_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
     b_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
     lengths = np.diff(cu).astype(np.float64)
@@ -643,6 +678,7 @@ def run_varlen(args, cfg):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -708,16 +744,7 @@ def run_f32(args, cfg):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    with no_gc():
-        t0 = time.perf_counter()
-        for ev in events:
-            step(ev)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    events, wall = timed_steps(args, stream, step, 3)
     f_ms = statistics.fmean(ev[0].elapsed_time(ev[1]) for ev in events)
     b_ms = statistics.fmean(ev[1].elapsed_time(ev[2]) for ev in events)
     f_fwd, f_bwd = flops(B, H, N, d, causal)
@@ -730,6 +757,7 @@ def run_f32(args, cfg):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": False,
         "scaling": "weak",
@@ -774,6 +802,13 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="before the warm-up, run the step back to back for this long (host time) so the "
+                         "timed steps see the clock the part holds under steady load, not the transient "
+                         "after idle; 0 turns it off")
+    ap.add_argument("--step-times", metavar="PATH", default=None,
+                    help="dense workloads: also write every timed step's per-kernel event times (ms) to PATH "
+                         "as JSON")
     ap.add_argument("--workload", default=DEFAULT,
                     choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS) + sorted(FP8_WORKLOADS)
                     + sorted(PREP_WORKLOADS) + sorted(VARLEN_WORKLOADS) + sorted(F32_WORKLOADS))
@@ -804,8 +839,8 @@ def main(argv=None):
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every box here has a single MI355X "
               "and this build has no multi-GPU path", file=sys.stderr)
         return 2
-    if args.steps <= 0 or args.warmup < 0:
-        print("--steps must be > 0 and --warmup >= 0", file=sys.stderr)
+    if args.steps <= 0 or args.warmup < 0 or args.settle_ms < 0:
+        print("--steps must be > 0, --warmup and --settle-ms >= 0", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -901,20 +936,7 @@ def main(argv=None):
         if ev is not None:
             ev[3].record(stream)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    with no_gc():
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(events[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    events, wall = timed_steps(args, stream, step, 4)
 
     per = {"fwd": [], "bwd_dkdv": [], "bwd_dq": [], "bwd": [], "step": []}
     for ev in events:
@@ -925,6 +947,9 @@ def main(argv=None):
             per["bwd_dq"].append(ev[1].elapsed_time(ev[2]))
             per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
     per = {k_: v_ for k_, v_ in per.items() if v_}
+    if args.step_times:
+        with open(args.step_times, "w") as f:
+            json.dump({"settle_ms": args.settle_ms, "warmup": args.warmup, "ms": per}, f)
     mean = {k_: statistics.fmean(v_) for k_, v_ in per.items()}
     med = {k_: statistics.median(v_) for k_, v_ in per.items()}
     low = {k_: min(v_) for k_, v_ in per.items()}
@@ -975,6 +1000,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -88,6 +88,14 @@ def test_cli_refuses_several_gpus_and_bad_counts(capsys):
     assert "one GPU only" in capsys.readouterr().err
     assert bench.main(["--steps", "0"]) == 2
     assert bench.main(["--warmup", "-1"]) == 2
+    assert bench.main(["--settle-ms", "-1"]) == 2
+
+
+def test_settle_off_touches_nothing():
+    """--settle-ms 0 runs no step (so the phase is off, not one step long)."""
+    calls = []
+    bench.settle(lambda: calls.append(1), None, 0)
+    assert calls == []
 
 
 def test_cpu_baseline_cores_are_the_affinity_set():
