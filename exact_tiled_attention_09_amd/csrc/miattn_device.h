@@ -241,12 +241,20 @@ __device__ __forceinline__ void wg_coords(int w, int nbh, int ntile, bool heavy_
 // (under a causal mask one head at a time would leave the heaviest tile of
 // the last head to start late: about 9% longer in a greedy-schedule model of
 // 16 heads x 16 tiles on 32 CUs, against none for groups of two or more).
+// With the XCD split, the group narrows until it divides an XCD's range: a
+// group that straddled two ranges would give one XCD the heavy tiles of its
+// heads and the next XCD the light ones (B1 H16 N16384 causal: two heads per
+// range, 3:1 work between neighbouring XCDs with groups of four).
 // The result is a bijection of [0, nbh*ntile).
 __host__ __device__ __forceinline__ void wg_coords_grouped(int w, int nbh, int ntile, int group,
                                                            bool heavy_last_tile, int& bh, int& t) {
   const int total = nbh * ntile;
   int g = w;
-  if ((total & 7) == 0) g = (w & 7) * (total >> 3) + (w >> 3);
+  if ((total & 7) == 0) {
+    g = (w & 7) * (total >> 3) + (w >> 3);
+    const int range = total >> 3;
+    while (group > 1 && range % (group * ntile) != 0) --group;
+  }
   const int per = group * ntile;
   const int grp = g / per;
   const int r = g - grp * per;
