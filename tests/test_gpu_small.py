@@ -78,6 +78,19 @@ def test_bf16_fwd_bwd_ragged(lib, N, d, causal):
     _check(out, ref, "bf16")
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 24, 768), (1, 40, 768), (2, 8, 1024)])
+def test_causal_order_with_narrowed_head_groups(lib, B, H, N):
+    """Shapes whose XCD ranges hold 3, 5 and 2 heads, so the causal query-tile
+    order narrows its group of four heads to 3, 1 and 2: every head of the
+    forward and the backward against the oracle."""
+    print(f"[case] narrowed head groups B={B} H={H} N={N}", flush=True)
+    inp = dense_inputs(B, H, N, 64, "bf16", seed=B * 100 + H)
+    scale = 1.0 / 8.0
+    out = _run_dense(lib, inp, scale, True, "bf16")
+    ref = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True)
+    _check(out, ref, "bf16")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 128, 200])
