@@ -117,10 +117,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(AttnArgs a, int n_
     kt = item & 0xffff;
     chunk = item >> 16;
   } else {
-    // the earliest key tiles carry the most work; packed sequences go
-    // tile-major over every (sequence, head) so that their very different
-    // lengths spread over the XCDs
-    if (VARLEN) wg_coords_tile_major(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);
+    // the earliest key tiles carry the most work; packed sequences: each XCD
+    // takes the same heads of every sequence, one (sequence, head) at a time
+    if (VARLEN) wg_coords_unit_major(blockIdx.x, a.B, a.Hkv, n_ktiles, bh, kt);
     else wg_coords(blockIdx.x, a.B * a.Hkv, n_ktiles, false, bh, kt);
   }
   const int G = a.H / a.Hkv;
@@ -554,9 +553,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   // causal masks, windows and block lists: groups of four heads per XCD,
   // heaviest tiles first in each group under a causal mask; plain non-causal:
   // all heads' tile 0, then all tile 1, ... (measured faster there)
-  // packed sequences: tile-major over every (sequence, head), heaviest first
-  // (as the forward), so sequences of very different lengths spread over XCDs
-  if (VARLEN) wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);
+  // packed sequences: each XCD takes the same heads of every sequence, one
+  // (sequence, head) at a time, heaviest tiles first (as the forward)
+  if (VARLEN) {
+    wg_coords_unit_major(blockIdx.x, a.B, a.H, n_qtiles, bh, tile);
+    if (CAUSAL) tile = n_qtiles - 1 - tile;
+  }
   else if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;

@@ -84,10 +84,14 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   // causal masks, windows and block lists: groups of four heads per XCD,
   // heaviest tiles first in each group under a causal mask; plain non-causal:
   // all heads' tile 0, then all tile 1, ... (measured faster there)
-  // packed sequences: every (sequence, head)'s tile t together, heaviest
-  // tiles first, so that sequences of very different lengths spread over
-  // all XCDs (a contiguous range per XCD would give one XCD the longest ones)
-  if (VARLEN) wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, CAUSAL, bh, tile);
+  // packed sequences: each XCD takes the same heads of every sequence (equal
+  // work whatever the lengths; a contiguous range of sequences per XCD would
+  // give one XCD the longest ones), one (sequence, head) at a time with its
+  // tiles together, heaviest first
+  if (VARLEN) {
+    wg_coords_unit_major(blockIdx.x, a.B, a.H, n_qtiles, bh, tile);
+    if (CAUSAL) tile = n_qtiles - 1 - tile;
+  }
   else if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;

@@ -215,6 +215,25 @@ __device__ __forceinline__ void wg_coords_tile_major(int w, int nbh, int ntile, 
   if (heavy_last_tile) t = ntile - 1 - t;
 }
 
+// Workgroup -> (sequence*head, tile) for packed sequences, nh heads each:
+// XCD x = w % 8 takes heads x*nh/8 .. (x+1)*nh/8 - 1 of every sequence (the
+// same work on every XCD, whatever the lengths; grouped query heads keep
+// their K/V head on one XCD) and works through them one (sequence, head) at a
+// time, all its tiles together, so that the operands its tiles share stay in
+// that XCD's L2.  With nh not a multiple of 8, tile-major.
+__host__ __device__ __forceinline__ void wg_coords_unit_major(int w, int nseq, int nh, int ntile, int& bh, int& t) {
+  if (nh % 8 != 0) {
+    bh = w % (nseq * nh);
+    t = w / (nseq * nh);
+    return;
+  }
+  const int x = w & 7, l = w >> 3, hx = nh >> 3;
+  const int u = l / ntile;
+  t = l - u * ntile;
+  const int seq = u / hx;
+  bh = seq * nh + x * hx + (u - seq * hx);
+}
+
 // Workgroup -> (sequence*head, tile).  Workgroups are dispatched to the 8 XCDs
 // in turn (w -> XCD w % 8), each XCD with its own L2.  When the grid divides by
 // 8, XCD x takes the contiguous logical range [x*total/8, (x+1)*total/8),

@@ -45,6 +45,37 @@ static int check(int nbh, int ntile, int group, bool heavy) {
   return 0;
 }
 
+// Packed sequences (wg_coords_unit_major): a bijection, and every XCD gets the
+// same heads of every sequence, so per-XCD work is equal for any lengths
+// (checked with sequence s costing s + 1 per tile, tile t costing t + 1).
+static int check_unit_major(int nseq, int nh, int ntile) {
+  const int total = nseq * nh * ntile;
+  std::vector<int> hit(total, 0);
+  std::vector<long long> work(8, 0);
+  for (int w = 0; w < total; ++w) {
+    int bh = -1, t = -1;
+    miattn::wg_coords_unit_major(w, nseq, nh, ntile, bh, t);
+    if (bh < 0 || bh >= nseq * nh || t < 0 || t >= ntile) {
+      std::printf("FAIL unit-major out of range: nseq %d nh %d ntile %d w %d -> (%d, %d)\n", nseq, nh, ntile, w, bh, t);
+      return 1;
+    }
+    hit[bh * ntile + t] += 1;
+    work[w % 8] += (long long)(bh / nh + 1) * (t + 1);
+  }
+  for (int i = 0; i < total; ++i)
+    if (hit[i] != 1) {
+      std::printf("FAIL unit-major not a bijection: nseq %d nh %d ntile %d\n", nseq, nh, ntile);
+      return 1;
+    }
+  if (nh % 8 == 0)
+    for (int x = 1; x < 8; ++x)
+      if (work[x] != work[0]) {
+        std::printf("FAIL unit-major unbalanced: nseq %d nh %d ntile %d\n", nseq, nh, ntile);
+        return 1;
+      }
+  return 0;
+}
+
 int main() {
   int fails = 0, cases = 0;
   const int heads[] = {1, 2, 3, 5, 8, 12, 16, 24, 32, 40, 64, 96, 128, 256};
@@ -56,6 +87,12 @@ int main() {
           fails += check(nbh, ntile, group, heavy);
           ++cases;
         }
+  for (int nseq : {1, 2, 3, 16, 33})
+    for (int nh : {1, 3, 8, 12, 16, 32, 64})
+      for (int ntile : {1, 2, 7, 32, 63}) {
+        fails += check_unit_major(nseq, nh, ntile);
+        ++cases;
+      }
   if (fails) {
     std::printf("%d of %d order checks failed\n", fails, cases);
     return 1;

@@ -1,8 +1,10 @@
-"""The query-tile workgroup order of the causal and masked passes
+"""The workgroup orders of the causal and masked query-tile passes
 (`wg_coords_grouped` in csrc/miattn_device.h), checked on the CPU by a host
 program built from the same header: a bijection for every shape, and equal
 causal work on every XCD whenever an XCD's range holds whole heads (a group
-of heads narrower than four when the range holds fewer)."""
+of heads narrower than four when the range holds fewer); and the packed-
+sequence order (`wg_coords_unit_major`): a bijection giving every XCD the
+same heads of every sequence, so equal work whatever the lengths."""
 import os
 import shutil
 import subprocess
