@@ -552,7 +552,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
   int bh, tile;
   // causal masks, windows and block lists: groups of four heads per XCD,
   // heaviest tiles first in each group under a causal mask; plain non-causal:
-  // all heads' tile 0, then all tile 1, ... (measured faster there)
+  // the same groups when a head has 4 or more query tiles (its K/V no longer
+  // fit in L2 for many heads at once), else all heads' tile 0, then all tile
+  // 1, ... (measured faster for 2 tiles a head)
   // packed sequences: each XCD takes the same heads of every sequence, one
   // (sequence, head) at a time, heaviest tiles first (as the forward)
   if (VARLEN) {
@@ -560,6 +562,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(AttnArgs a, int n_qt
     if (CAUSAL) tile = n_qtiles - 1 - tile;
   }
   else if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
+  else if (n_qtiles >= 4) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, false, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;

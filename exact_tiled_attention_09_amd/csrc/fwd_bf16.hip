@@ -83,7 +83,9 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
   int bh, tile;
   // causal masks, windows and block lists: groups of four heads per XCD,
   // heaviest tiles first in each group under a causal mask; plain non-causal:
-  // all heads' tile 0, then all tile 1, ... (measured faster there)
+  // the same groups when a head has 4 or more query tiles (its K/V no longer
+  // fit in L2 for many heads at once), else all heads' tile 0, then all tile
+  // 1, ... (measured faster for 2 tiles a head)
   // packed sequences: each XCD takes the same heads of every sequence (equal
   // work whatever the lengths; a contiguous range of sequences per XCD would
   // give one XCD the longest ones), one (sequence, head) at a time with its
@@ -93,6 +95,7 @@ __global__ void __launch_bounds__(512, 1) fwd_stag_kernel(AttnArgs a, int n_qtil
     if (CAUSAL) tile = n_qtiles - 1 - tile;
   }
   else if (CAUSAL || MASK != kMaskPlain) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, CAUSAL, bh, tile);
+  else if (n_qtiles >= 4) wg_coords_grouped(blockIdx.x, a.B * a.H, n_qtiles, 4, false, bh, tile);
   else wg_coords_tile_major(blockIdx.x, a.B * a.H, n_qtiles, false, bh, tile);
   const int b = bh / a.H;
   const int h = bh - b * a.H;

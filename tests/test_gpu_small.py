@@ -78,16 +78,18 @@ def test_bf16_fwd_bwd_ragged(lib, N, d, causal):
     _check(out, ref, "bf16")
 
 
-@pytest.mark.parametrize("B,H,N", [(1, 24, 768), (1, 40, 768), (2, 8, 1024)])
-def test_causal_order_with_narrowed_head_groups(lib, B, H, N):
-    """Shapes whose XCD ranges hold 3, 5 and 2 heads, so the causal query-tile
-    order narrows its group of four heads to 3, 1 and 2: every head of the
-    forward and the backward against the oracle."""
-    print(f"[case] narrowed head groups B={B} H={H} N={N}", flush=True)
+@pytest.mark.parametrize("B,H,N,causal", [(1, 24, 768, True), (1, 40, 768, True), (2, 8, 1024, True),
+                                          (1, 24, 1100, False), (2, 8, 1024, False)])
+def test_order_with_narrowed_head_groups(lib, B, H, N, causal):
+    """Shapes whose XCD ranges hold 3, 5 and 2 heads, so the query-tile order
+    narrows its group of four heads to 3, 1 and 2 (non-causal passes group
+    heads from 4 query tiles a head on, here with a ragged last tile): every
+    head of the forward and the backward against the oracle."""
+    print(f"[case] narrowed head groups B={B} H={H} N={N} causal={causal}", flush=True)
     inp = dense_inputs(B, H, N, 64, "bf16", seed=B * 100 + H)
     scale = 1.0 / 8.0
-    out = _run_dense(lib, inp, scale, True, "bf16")
-    ref = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True)
+    out = _run_dense(lib, inp, scale, causal, "bf16")
+    ref = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal)
     _check(out, ref, "bf16")
 
 
