@@ -18,7 +18,7 @@ Definition followed (per batch b, head h; or per packed sequence s, head h):
 A query row with no visible key is defined as O = 0, LSE = -inf and contributes
 no gradient [P3 §04, the all-masked-row convention].
 
-Readings where the pages are loose (each is listed in the design doc):
+Readings where the pages are loose:
   * ``scale`` multiplies Q K^T and is an argument (1/sqrt(d) in every workload);
     LSE is that of the scaled scores and dQ, dK carry one factor of ``scale``.
   * LSE uses the natural logarithm.

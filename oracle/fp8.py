@@ -8,7 +8,7 @@ normal 2^-6) with dynamic per-block scales computed for each load block of Q
 and of K, s = max|X_block| / 448, X_fp8 = E4M3(X / s); S = Q K^T accumulates
 in fp32, the softmax runs in fp32, and O is dequantized to bf16.
 
-Readings (each listed in the design doc):
+Readings where the pages leave the format open:
   * E4M3 is the OCP "E4M3FN" encoding: exponent bias 7, no infinities, the
     all-ones exponent and mantissa pattern is NaN, subnormals below 2^-6.
   * Conversion rounds to nearest, ties to even, keeping the sign of zero;
